@@ -1,0 +1,105 @@
+"""Seeded synthetic inputs for the sequence-parallel region, and the workloads.
+
+This module only draws numbers; it holds none of the region's arithmetic.
+It is shared by the oracle-side and the GPU-side checks so that both read
+identical bits.
+
+Recipe (the pages measure on no dataset; activations are synthetic by nature):
+  numpy.random.default_rng(seed) (PCG64), standard_normal in float32, drawn
+  in this fixed order over the FULL [s, b, h] tensor (rows = s*b, row-major):
+    x (the reduced row-parallel output), residual, dy (gradient of y),
+    [dh_out], bias * 0.02, beta * 0.02, gamma = 1 + 0.02 * noise.
+  "N(0, 0.02)" is read as standard deviation 0.02.  bf16 tensors are the
+  round-to-nearest-even bfloat16 of those float32 draws, made by torch's
+  float32 -> bfloat16 conversion, and travel as raw uint16 bit patterns.
+  Shard i of t is rows [i*s/t*b, (i+1)*s/t*b) of the full tensor (the
+  sequence-major layout makes a shard one contiguous slab).
+"""
+from dataclasses import dataclass, field
+
+import numpy as np
+
+F32, BF16 = 0, 1
+LAYERNORM, RMSNORM = 0, 1
+
+
+def to_bf16_bits(a32):
+    """float32 array -> raw bfloat16 patterns (uint16), RNE, via torch."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a32, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def make_inputs(rows, h, io, seed=0, dh_out=False):
+    """Draws every input of one region call over `rows` token rows of width h.
+
+    Returns a dict of numpy arrays: x, residual, dy, dh_out (or None) in the
+    I/O type (float32 or uint16 bf16 bits), and bias, beta, gamma in float32.
+    """
+    rng = np.random.default_rng(seed)
+    n = rows * h
+    std = lambda k: rng.standard_normal(k, dtype=np.float32)
+    x, residual, dy = std(n), std(n), std(n)
+    dho = std(n) if dh_out else None
+    bias = std(h) * np.float32(0.02)
+    beta = std(h) * np.float32(0.02)
+    gamma = np.float32(1.0) + std(h) * np.float32(0.02)
+    cast = to_bf16_bits if io == BF16 else (lambda a: a)
+    return {"x": cast(x), "residual": cast(residual), "dy": cast(dy),
+            "dh_out": None if dho is None else cast(dho),
+            "bias": bias, "beta": beta, "gamma": gamma}
+
+
+@dataclass
+class Workload:
+    """One shard shape and region setting (sizes as the pages' layers)."""
+    name: str
+    s: int                 # full sequence length
+    b: int                 # batch
+    h: int                 # hidden size
+    t: int                 # sequence/tensor-parallel degree
+    io: int                # F32 or BF16
+    norm: int              # LAYERNORM or RMSNORM
+    p: float               # dropout probability
+    eps: float
+    a: int = 0             # attention heads (accounting only)
+    seed: int = 0
+    calls_per_layer: int = 1
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def s_local(self):
+        return self.s // self.t
+
+    @property
+    def rows(self):        # N = s/t * b token rows in one shard
+        return self.s_local * self.b
+
+    @property
+    def elems(self):
+        return self.rows * self.h
+
+
+WORKLOADS = {
+    # A tiny fp32 shard for exhaustive checks: [64, 2, 256] of [128, 2, 256].
+    "tiny_fp32_t2": Workload("tiny_fp32_t2", s=128, b=2, h=256, t=2, io=F32,
+                             norm=LAYERNORM, p=0.1, eps=1e-5),
+    # 22B-class layer boundary (one layer of a 22B model): shard [256, 4, 6144].
+    "22b_h6144_t8": Workload("22b_h6144_t8", s=2048, b=4, h=6144, t=8, io=BF16,
+                             norm=LAYERNORM, p=0.1, eps=1e-5, a=64),
+    # 175B-class (GPT-3-scale) layer boundary: shard [256, 8, 12288], two
+    # region calls per layer (pre-attention and pre-MLP).
+    "175b_h12288_t8": Workload("175b_h12288_t8", s=2048, b=8, h=12288, t=8, io=BF16,
+                               norm=LAYERNORM, p=0.1, eps=1e-5, a=96, calls_per_layer=2),
+    # Long-sequence RMSNorm variant: shard [4096, 1, 8192].
+    "longseq_rms_h8192_t8_p0.1": Workload("longseq_rms_h8192_t8_p0.1", s=32768, b=1, h=8192,
+                                          t=8, io=BF16, norm=RMSNORM, p=0.1, eps=1e-6),
+    "longseq_rms_h8192_t8_p0": Workload("longseq_rms_h8192_t8_p0", s=32768, b=1, h=8192,
+                                        t=8, io=BF16, norm=RMSNORM, p=0.0, eps=1e-6),
+    # 1T-class wide rows, shard-size sweep t in {1, 2, 4, 8}: [2048/t, 4, 25600].
+    **{f"1t_h25600_t{t}": Workload(f"1t_h25600_t{t}", s=2048, b=4, h=25600, t=t, io=BF16,
+                                   norm=LAYERNORM, p=0.1, eps=1e-5, a=160, calls_per_layer=2)
+       for t in (1, 2, 4, 8)},
+}
+
+HEADLINE = "22b_h6144_t8"
