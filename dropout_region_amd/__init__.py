@@ -1,0 +1,210 @@
+"""Python binding of libsp_region.so (include/sp_region.h).
+
+Argument marshalling only: every step of the region runs in the library's
+HIP kernels.  The functions carry the C names and take torch tensors (or
+None) for the pointer arguments; torch provides device memory and the
+current HIP stream.  There is no fallback: if the library is not built,
+every call raises.
+"""
+import ctypes
+import os
+from dataclasses import dataclass
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsp_region.so")
+
+SPR_OK, SPR_ERR_INVALID_ARG, SPR_ERR_UNSUPPORTED, SPR_ERR_WORKSPACE, SPR_ERR_HIP = range(5)
+SPR_F32, SPR_BF16 = 0, 1
+SPR_LAYERNORM, SPR_RMSNORM = 0, 1
+
+
+class SprError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn}: {sp_region_status_string(status)} (status {status})")
+
+
+class spr_desc(ctypes.Structure):
+    _fields_ = [("s_local", ctypes.c_int64), ("b", ctypes.c_int64), ("h", ctypes.c_int64),
+                ("shard_index", ctypes.c_int32), ("t", ctypes.c_int32),
+                ("io", ctypes.c_int32), ("norm", ctypes.c_int32),
+                ("p", ctypes.c_float), ("eps", ctypes.c_float),
+                ("seed", ctypes.c_uint64), ("offset", ctypes.c_uint64)]
+
+
+@dataclass
+class Desc:
+    """Shard [s_local, b, h] of rank shard_index of t, and region settings."""
+    s_local: int
+    b: int
+    h: int
+    shard_index: int = 0
+    t: int = 1
+    io: int = SPR_BF16
+    norm: int = SPR_LAYERNORM
+    p: float = 0.0
+    eps: float = 1e-5
+    seed: int = 0
+    offset: int = 0
+
+    @property
+    def rows(self):
+        return self.s_local * self.b
+
+    def c(self):
+        return spr_desc(self.s_local, self.b, self.h, self.shard_index, self.t, self.io,
+                        self.norm, self.p, self.eps, self.seed, self.offset)
+
+
+_lib = None
+
+
+def lib():
+    """The loaded HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"HIP library not built: {LIB_PATH} is missing "
+                               "(run __graft_entry__.build() or dropout_region_amd/build.py)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, D = ctypes.c_void_p, ctypes.POINTER(spr_desc)
+        L.sp_region_fwd.argtypes = [D] + [P] * 10 + [P]
+        L.sp_region_fwd.restype = ctypes.c_int
+        L.sp_region_bwd.argtypes = [D] + [P] * 12 + [P, ctypes.c_size_t, P]
+        L.sp_region_bwd.restype = ctypes.c_int
+        L.sp_region_bwd_workspace_bytes.argtypes = [D]
+        L.sp_region_bwd_workspace_bytes.restype = ctypes.c_size_t
+        L.sp_region_activation_bytes.argtypes = [D, P, P]
+        L.sp_region_activation_bytes.restype = ctypes.c_int
+        L.sp_region_status_string.argtypes = [ctypes.c_int]
+        L.sp_region_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+# ------------------------------------------------------------ marshalling
+def _io_dtype(d):
+    import torch
+    return torch.bfloat16 if d.io == SPR_BF16 else torch.float32
+
+
+def _arg(t, name, numel, dtype, device, optional=False):
+    """Device pointer of tensor t after checking what the C side cannot:
+    device, dtype, contiguity and size."""
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda or (device is not None and t.device != device):
+        raise ValueError(f"{name} must be on {device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, want {dtype}")
+    if not t.is_contiguous() or t.numel() != numel:
+        raise ValueError(f"{name}: want a contiguous tensor of {numel} elements")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+# ------------------------------------------------------------ entry points
+def sp_region_status_string(status):
+    return lib().sp_region_status_string(int(status)).decode()
+
+
+def sp_region_activation_bytes(d):
+    """(saved_for_bwd, retained_output) bytes of one forward call."""
+    a, b = ctypes.c_uint64(), ctypes.c_uint64()
+    st = lib().sp_region_activation_bytes(ctypes.byref(d.c()), ctypes.byref(a), ctypes.byref(b))
+    if st != SPR_OK:
+        raise SprError("sp_region_activation_bytes", st)
+    return a.value, b.value
+
+
+def sp_region_bwd_workspace_bytes(d):
+    return int(lib().sp_region_bwd_workspace_bytes(ctypes.byref(d.c())))
+
+
+def sp_region_fwd(d, x, bias, residual, gamma, beta, h_out, y_out, mask_out, mean_out,
+                  rstd_out, stream=None):
+    import torch
+    L = lib()
+    N, H, io, dev = d.rows, d.h, _io_dtype(d), x.device if x is not None else None
+    f32, u8 = torch.float32, torch.uint8
+    args = [_arg(x, "x", N * H, io, dev), _arg(bias, "bias", H, f32, dev, True),
+            _arg(residual, "residual", N * H, io, dev), _arg(gamma, "gamma", H, f32, dev),
+            _arg(beta, "beta", H, f32, dev, True), _arg(h_out, "h_out", N * H, io, dev),
+            _arg(y_out, "y_out", N * H, io, dev), _arg(mask_out, "mask_out", N * H, u8, dev, True),
+            _arg(mean_out, "mean_out", N, f32, dev, True), _arg(rstd_out, "rstd_out", N, f32, dev)]
+    st = L.sp_region_fwd(ctypes.byref(d.c()), *args, _stream(stream))
+    if st != SPR_OK:
+        raise SprError("sp_region_fwd", st)
+
+
+def sp_region_bwd(d, dy, dh_out, h, mask, mean, rstd, gamma, dx_out, dres_out, dgamma_out,
+                  dbeta_out, dbias_out, workspace, stream=None):
+    import torch
+    L = lib()
+    N, H, io, dev = d.rows, d.h, _io_dtype(d), dy.device if dy is not None else None
+    f32, u8 = torch.float32, torch.uint8
+    if workspace is None or not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    args = [_arg(dy, "dy", N * H, io, dev), _arg(dh_out, "dh_out", N * H, io, dev, True),
+            _arg(h, "h", N * H, io, dev), _arg(mask, "mask", N * H, u8, dev, True),
+            _arg(mean, "mean", N, f32, dev, True), _arg(rstd, "rstd", N, f32, dev),
+            _arg(gamma, "gamma", H, f32, dev), _arg(dx_out, "dx_out", N * H, io, dev),
+            _arg(dres_out, "dres_out", N * H, io, dev),
+            _arg(dgamma_out, "dgamma_out", H, f32, dev),
+            _arg(dbeta_out, "dbeta_out", H, f32, dev, True),
+            _arg(dbias_out, "dbias_out", H, f32, dev, True)]
+    st = L.sp_region_bwd(ctypes.byref(d.c()), *args, ctypes.c_void_p(workspace.data_ptr()),
+                         ctypes.c_size_t(ws_bytes), _stream(stream))
+    if st != SPR_OK:
+        raise SprError("sp_region_bwd", st)
+
+
+# ------------------------------------------------------------ allocation helpers
+def alloc_fwd_outputs(d, device):
+    """torch.empty outputs of sp_region_fwd: h, y, mask, mean, rstd."""
+    import torch
+    N, H, io = d.rows, d.h, _io_dtype(d)
+    e = lambda n, dt: torch.empty(n, dtype=dt, device=device)
+    return {"h": e(N * H, io), "y": e(N * H, io),
+            "mask": e(N * H, torch.uint8) if d.p > 0 else None,
+            "mean": e(N, torch.float32) if d.norm == SPR_LAYERNORM else None,
+            "rstd": e(N, torch.float32)}
+
+
+def alloc_bwd_outputs(d, device, want_dbias=True):
+    """torch.empty outputs of sp_region_bwd and a zero-filled workspace."""
+    import torch
+    N, H, io = d.rows, d.h, _io_dtype(d)
+    e = lambda n, dt: torch.empty(n, dtype=dt, device=device)
+    ws = max(sp_region_bwd_workspace_bytes(d), 16)
+    return {"dx": e(N * H, io), "dres": e(N * H, io), "dgamma": e(H, torch.float32),
+            "dbeta": e(H, torch.float32) if d.norm == SPR_LAYERNORM else None,
+            "dbias": e(H, torch.float32) if want_dbias else None,
+            "workspace": torch.zeros(ws, dtype=torch.uint8, device=device)}
+
+
+def fwd(d, x, bias, residual, gamma, beta, stream=None):
+    """Allocates the outputs and runs sp_region_fwd; returns them as a dict."""
+    o = alloc_fwd_outputs(d, x.device)
+    sp_region_fwd(d, x, bias, residual, gamma, beta, o["h"], o["y"], o["mask"], o["mean"],
+                  o["rstd"], stream)
+    return o
+
+
+def bwd(d, dy, dh_out, h, mask, mean, rstd, gamma, want_dbias=True, stream=None):
+    """Allocates the outputs and runs sp_region_bwd; returns them as a dict."""
+    o = alloc_bwd_outputs(d, dy.device, want_dbias)
+    sp_region_bwd(d, dy, dh_out, h, mask, mean, rstd, gamma, o["dx"], o["dres"], o["dgamma"],
+                  o["dbeta"], o["dbias"], o["workspace"], stream)
+    return o

@@ -1,0 +1,92 @@
+// sp_plan.h -- launch plans and kernel argument blocks (host and device).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "sp_region.h"
+
+namespace spr {
+
+// How one row of h elements is spread over threads.  A row is cut into
+// 16-byte vectors (8 bf16 or 4 fp32 elements); thread `tid` of the row's
+// team owns vectors tid, tid + tpr, ..., tid + (vpt-1)*tpr, so each load
+// instruction of a wave covers 1 KiB of contiguous memory.
+struct RowPlan {
+    int epv;        // elements per vector (8 bf16, 4 fp32)
+    int nvec;       // vectors per row, h / epv
+    int vpt;        // vectors per thread (compile-time in the kernels)
+    int tpr;        // threads per row team (multiple of 64)
+    int rpw;        // row teams per workgroup (4 one-wave teams, or 1)
+    int block;      // threads per workgroup = tpr * rpw
+    int lb;         // the kernel's launch bound (>= block): caps VGPRs per wave
+};
+
+// The (vectors per thread, launch bound) pairs compiled for whole-workgroup
+// rows.  A bound of 1024 threads leaves 128 VGPRs per wave, 768 leaves 168,
+// 512 leaves 256; more vectors per thread need more registers.
+struct VptBound {
+    int vpt, lb;
+};
+static constexpr VptBound kWgCombos[] = {{1, 1024}, {2, 1024}, {3, 1024}, {4, 1024},
+                                         {5, 768},  {6, 768},  {8, 512}};
+
+enum PlanKind { kPlanForward, kPlanBackward };
+
+// Picks a row plan for h; false if h is unsupported.  The forward prefers
+// about four vectors per thread, the backward (which keeps three column
+// accumulators per element) as few as possible.
+bool make_row_plan(int io, int64_t h, PlanKind kind, RowPlan* plan);
+
+struct FwdArgs {
+    const void* x;
+    const float* bias;
+    const void* residual;
+    const float* gamma;
+    const float* beta;
+    void* h_out;
+    void* y_out;
+    uint8_t* mask_out;
+    float* mean_out;
+    float* rstd_out;
+    int64_t rows;          // N
+    int64_t hidden;        // h
+    uint64_t row_base;     // shard_index * N: global index of this shard's row 0
+    uint32_t key_lo, key_hi, off_lo, off_hi;
+    uint32_t thr;          // floor(p * 2^32)
+    float scale;           // fp32(1 / (1 - p))
+    float inv_h;           // 1 / h
+    float eps;
+    int nvec;
+};
+
+struct BwdArgs {
+    const void* dy;
+    const void* dh_out;
+    const void* h;
+    const uint8_t* mask;
+    const float* mean;
+    const float* rstd;
+    const float* gamma;
+    void* dx_out;
+    void* dres_out;
+    float* partials;       // [teams][3][h] fp32 column partials
+    float* dgamma_out;
+    float* dbeta_out;
+    float* dbias_out;
+    int64_t rows;
+    int64_t hidden;
+    float scale;
+    float inv_h;
+    int nvec;
+    int teams;             // row teams in the grid = partial rows
+};
+
+hipError_t launch_fwd(const spr_desc& d, const RowPlan& plan, const FwdArgs& a, hipStream_t s);
+
+// Number of row teams (= fp32 partial rows) the backward uses for this desc.
+int64_t bwd_teams(const spr_desc& d, const RowPlan& plan);
+hipError_t launch_bwd(const spr_desc& d, const RowPlan& plan, const BwdArgs& a, hipStream_t s);
+
+}  // namespace spr

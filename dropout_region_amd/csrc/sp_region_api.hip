@@ -1,0 +1,260 @@
+// sp_region_api.hip -- the C ABI of include/sp_region.h: host-side argument
+// checks, launch planning and dispatch.  Every check runs before the first
+// HIP call, so an invalid call launches nothing and touches no output.
+#include <math.h>
+#include <stdint.h>
+
+#include "sp_plan.h"
+#include "sp_region.h"
+
+namespace spr {
+
+bool make_row_plan(int io, int64_t h, PlanKind kind, RowPlan* plan) {
+    const int epv = (io == SPR_BF16) ? 8 : 4;
+    if (h <= 0 || h % epv != 0) return false;
+    const int64_t nvec = h / epv;
+    RowPlan p{};
+    p.epv = epv;
+    p.nvec = (int)nvec;
+    if (nvec <= 4 * 64) {                    // short rows: one wave per row, 4 rows per WG
+        p.vpt = (int)((nvec + 63) / 64);
+        p.tpr = 64;
+        p.rpw = 4;
+        p.block = 256;
+        p.lb = 256;
+        *plan = p;
+        return true;
+    }
+    // One workgroup per row.  Take the first candidate (in preference order)
+    // whose split leaves no vector slot idle, else the one wasting fewest.
+    static const int kFwdOrder[] = {4, 3, 5, 6, 2, 8, 1};
+    static const int kBwdOrder[] = {1, 2, 3, 4, 5, 6, 8};
+    const int* order = (kind == kPlanForward) ? kFwdOrder : kBwdOrder;
+    int best_vpt = 0, best_lb = 0;
+    int64_t best_tpr = 0, best_waste = INT64_MAX;
+    for (int i = 0; i < 7; ++i) {
+        const int v = order[i];
+        int lb = 0;
+        for (const VptBound& c : kWgCombos)
+            if (c.vpt == v) lb = c.lb;
+        const int64_t tpr = ((nvec + v - 1) / v + 63) / 64 * 64;
+        if (tpr > lb) continue;
+        const int64_t waste = tpr * v - nvec;
+        if (waste < best_waste) {
+            best_waste = waste;
+            best_vpt = v;
+            best_lb = lb;
+            best_tpr = tpr;
+        }
+    }
+    if (best_vpt == 0) return false;
+    p.vpt = best_vpt;
+    p.tpr = (int)best_tpr;
+    p.rpw = 1;
+    p.block = p.tpr;
+    p.lb = best_lb;
+    *plan = p;
+    return true;
+}
+
+}  // namespace spr
+
+using namespace spr;
+
+namespace {
+
+struct Range {
+    uintptr_t lo, hi;   // [lo, hi); empty when lo == hi
+};
+
+Range range_of(const void* p, uint64_t bytes) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    return p ? Range{a, a + (uintptr_t)bytes} : Range{0, 0};
+}
+
+bool overlaps(Range a, Range b) {
+    if (a.lo == a.hi || b.lo == b.hi) return false;
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+// Outputs must not overlap each other or any input.
+bool disjoint(const Range* outs, int nout, const Range* ins, int nin) {
+    for (int i = 0; i < nout; ++i) {
+        for (int j = i + 1; j < nout; ++j)
+            if (overlaps(outs[i], outs[j])) return false;
+        for (int j = 0; j < nin; ++j)
+            if (overlaps(outs[i], ins[j])) return false;
+    }
+    return true;
+}
+
+// Field checks shared by every entry point.
+spr_status check_fields(const spr_desc* d) {
+    if (!d) return SPR_ERR_INVALID_ARG;
+    if (d->s_local < 1 || d->b < 1 || d->h < 1) return SPR_ERR_INVALID_ARG;
+    if (d->t < 1 || d->shard_index < 0 || d->shard_index >= d->t) return SPR_ERR_INVALID_ARG;
+    if (d->io != SPR_F32 && d->io != SPR_BF16) return SPR_ERR_INVALID_ARG;
+    if (d->norm != SPR_LAYERNORM && d->norm != SPR_RMSNORM) return SPR_ERR_INVALID_ARG;
+    if (!(d->p >= 0.0f && d->p < 1.0f)) return SPR_ERR_INVALID_ARG;      // also rejects NaN
+    if (!(d->eps > 0.0f) || isinf(d->eps)) return SPR_ERR_INVALID_ARG;
+    // N*h and the global element index (t*N*h) must fit comfortably in 63 bits.
+    if (d->s_local > (INT64_C(1) << 40) / d->b) return SPR_ERR_UNSUPPORTED;
+    const int64_t rows = d->s_local * d->b;
+    if ((double)rows * (double)d->h * (double)d->t > 9.0e18) return SPR_ERR_UNSUPPORTED;
+    return SPR_OK;
+}
+
+// Field checks plus what the kernels handle; fills the launch plan.
+spr_status check_desc(const spr_desc* d, RowPlan* plan, PlanKind kind) {
+    const spr_status st = check_fields(d);
+    if (st != SPR_OK) return st;
+    if (d->s_local * d->b > INT32_MAX) return SPR_ERR_UNSUPPORTED;
+    if (d->h / (d->io == SPR_BF16 ? 8 : 4) > 4096) return SPR_ERR_UNSUPPORTED;
+    if (!make_row_plan(d->io, d->h, kind, plan)) return SPR_ERR_UNSUPPORTED;
+    return SPR_OK;
+}
+
+size_t workspace_bytes(const spr_desc* d, const RowPlan& plan) {
+    const uint64_t bytes = (uint64_t)bwd_teams(*d, plan) * 3u * (uint64_t)d->h * sizeof(float);
+    return (size_t)((bytes + 255u) & ~(uint64_t)255u);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sp_region_status_string(spr_status s) {
+    switch (s) {
+        case SPR_OK: return "ok";
+        case SPR_ERR_INVALID_ARG: return "invalid argument";
+        case SPR_ERR_UNSUPPORTED: return "unsupported shape";
+        case SPR_ERR_WORKSPACE: return "workspace missing or too small";
+        case SPR_ERR_HIP: return "HIP error";
+    }
+    return "unknown status";
+}
+
+spr_status sp_region_activation_bytes(const spr_desc* d, uint64_t* saved_for_bwd,
+                                      uint64_t* retained_output) {
+    const spr_status st = check_fields(d);
+    if (st != SPR_OK) return st;
+    if (!saved_for_bwd || !retained_output) return SPR_ERR_INVALID_ARG;
+    const uint64_t rows = (uint64_t)(d->s_local * d->b);
+    const uint64_t elems = rows * (uint64_t)d->h;
+    const uint64_t io_bytes = (d->io == SPR_BF16) ? 2u : 4u;
+    const uint64_t h_bytes = elems * io_bytes;                       // the norm input h
+    const uint64_t mask = (d->p > 0.0f) ? elems : 0u;                // 1 byte per element
+    const uint64_t stats = rows * ((d->norm == SPR_LAYERNORM) ? 2u : 1u) * sizeof(float);
+    *saved_for_bwd = h_bytes + mask + stats;
+    *retained_output = elems * io_bytes;                             // y, the next block's input
+    return SPR_OK;
+}
+
+size_t sp_region_bwd_workspace_bytes(const spr_desc* d) {
+    RowPlan plan;
+    if (check_desc(d, &plan, kPlanBackward) != SPR_OK) return 0;
+    return workspace_bytes(d, plan);
+}
+
+spr_status sp_region_fwd(const spr_desc* d, const void* x, const float* bias,
+                         const void* residual, const float* gamma, const float* beta,
+                         void* h_out, void* y_out, uint8_t* mask_out, float* mean_out,
+                         float* rstd_out, hipStream_t stream) {
+    RowPlan plan;
+    spr_status st = check_desc(d, &plan, kPlanForward);
+    if (st != SPR_OK) return st;
+    const bool ln = d->norm == SPR_LAYERNORM, drop = d->p > 0.0f;
+    if (!x || !residual || !gamma || !h_out || !y_out || !rstd_out) return SPR_ERR_INVALID_ARG;
+    if (ln != (beta != nullptr) || ln != (mean_out != nullptr)) return SPR_ERR_INVALID_ARG;
+    if (drop && !mask_out) return SPR_ERR_INVALID_ARG;
+    if (!drop) mask_out = nullptr;                                   // ignored at p == 0
+    const void* io16[] = {x, residual, h_out, y_out};
+    for (const void* p : io16)
+        if (!aligned(p, 16)) return SPR_ERR_INVALID_ARG;
+    if (!aligned(bias, 16) || !aligned(gamma, 16) || !aligned(beta, 16)) return SPR_ERR_INVALID_ARG;
+    if (!aligned(mask_out, 8) || !aligned(mean_out, 4) || !aligned(rstd_out, 4))
+        return SPR_ERR_INVALID_ARG;
+
+    const int64_t rows = d->s_local * d->b;
+    const uint64_t E = (uint64_t)rows * (uint64_t)d->h;
+    const uint64_t es = (d->io == SPR_BF16) ? 2u : 4u;
+    const uint64_t pb = (uint64_t)d->h * 4u, sb = (uint64_t)rows * 4u;
+    const Range outs[] = {range_of(h_out, E * es), range_of(y_out, E * es), range_of(mask_out, E),
+                          range_of(mean_out, sb), range_of(rstd_out, sb)};
+    const Range ins[] = {range_of(x, E * es), range_of(residual, E * es), range_of(bias, pb),
+                         range_of(gamma, pb), range_of(beta, pb)};
+    if (!disjoint(outs, 5, ins, 5)) return SPR_ERR_INVALID_ARG;
+
+    FwdArgs a{};
+    a.x = x; a.bias = bias; a.residual = residual; a.gamma = gamma; a.beta = beta;
+    a.h_out = h_out; a.y_out = y_out; a.mask_out = mask_out; a.mean_out = mean_out;
+    a.rstd_out = rstd_out;
+    a.rows = rows;
+    a.hidden = d->h;
+    a.row_base = (uint64_t)d->shard_index * (uint64_t)rows;
+    a.key_lo = (uint32_t)d->seed;
+    a.key_hi = (uint32_t)(d->seed >> 32);
+    a.off_lo = (uint32_t)d->offset;
+    a.off_hi = (uint32_t)(d->offset >> 32);
+    // keep iff word >= floor(p * 2^32); p * 2^32 is exact in double
+    a.thr = (uint32_t)floor((double)d->p * 4294967296.0);
+    a.scale = (float)(1.0 / (1.0 - (double)d->p));
+    a.inv_h = (float)(1.0 / (double)d->h);
+    a.eps = d->eps;
+    a.nvec = plan.nvec;
+    return launch_fwd(*d, plan, a, stream) == hipSuccess ? SPR_OK : SPR_ERR_HIP;
+}
+
+spr_status sp_region_bwd(const spr_desc* d, const void* dy, const void* dh_out, const void* h,
+                         const uint8_t* mask, const float* mean, const float* rstd,
+                         const float* gamma, void* dx_out, void* dres_out, float* dgamma_out,
+                         float* dbeta_out, float* dbias_out, void* workspace,
+                         size_t workspace_bytes_given, hipStream_t stream) {
+    RowPlan plan;
+    spr_status st = check_desc(d, &plan, kPlanBackward);
+    if (st != SPR_OK) return st;
+    const bool ln = d->norm == SPR_LAYERNORM, drop = d->p > 0.0f;
+    if (!dy || !h || !rstd || !gamma || !dx_out || !dres_out || !dgamma_out)
+        return SPR_ERR_INVALID_ARG;
+    if (ln != (mean != nullptr) || ln != (dbeta_out != nullptr)) return SPR_ERR_INVALID_ARG;
+    if (drop && !mask) return SPR_ERR_INVALID_ARG;
+    if (!drop) mask = nullptr;
+    const void* io16[] = {dy, dh_out, h, dx_out, dres_out, gamma};
+    for (const void* p : io16)
+        if (!aligned(p, 16)) return SPR_ERR_INVALID_ARG;
+    if (!aligned(mask, 8) || !aligned(mean, 4) || !aligned(rstd, 4) || !aligned(dgamma_out, 4) ||
+        !aligned(dbeta_out, 4) || !aligned(dbias_out, 4))
+        return SPR_ERR_INVALID_ARG;
+    const size_t need = workspace_bytes(d, plan);
+    if (!workspace || workspace_bytes_given < need || !aligned(workspace, 16))
+        return SPR_ERR_WORKSPACE;
+
+    const int64_t rows = d->s_local * d->b;
+    const uint64_t E = (uint64_t)rows * (uint64_t)d->h;
+    const uint64_t es = (d->io == SPR_BF16) ? 2u : 4u;
+    const uint64_t pb = (uint64_t)d->h * 4u, sb = (uint64_t)rows * 4u;
+    const Range outs[] = {range_of(dx_out, E * es), range_of(dres_out, E * es),
+                          range_of(dgamma_out, pb), range_of(dbeta_out, pb),
+                          range_of(dbias_out, pb), range_of(workspace, need)};
+    const Range ins[] = {range_of(dy, E * es), range_of(dh_out, E * es), range_of(h, E * es),
+                         range_of(mask, E), range_of(mean, sb), range_of(rstd, sb),
+                         range_of(gamma, pb)};
+    if (!disjoint(outs, 6, ins, 7)) return SPR_ERR_INVALID_ARG;
+
+    BwdArgs a{};
+    a.dy = dy; a.dh_out = dh_out; a.h = h; a.mask = mask; a.mean = mean; a.rstd = rstd;
+    a.gamma = gamma; a.dx_out = dx_out; a.dres_out = dres_out;
+    a.partials = static_cast<float*>(workspace);
+    a.dgamma_out = dgamma_out; a.dbeta_out = dbeta_out; a.dbias_out = dbias_out;
+    a.rows = rows;
+    a.hidden = d->h;
+    a.scale = (float)(1.0 / (1.0 - (double)d->p));
+    a.inv_h = (float)(1.0 / (double)d->h);
+    a.nvec = plan.nvec;
+    a.teams = (int)bwd_teams(*d, plan);
+    return launch_bwd(*d, plan, a, stream) == hipSuccess ? SPR_OK : SPR_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,177 @@
+/*
+ * sp_region.h -- C ABI of the MI355X (gfx950) sequence-parallel region library.
+ *
+ * One rank's token shard [s/t, b, h] of a transformer layer's block-boundary
+ * activation goes through the band that Megatron-style sequence parallelism
+ * shards along the sequence: the reduced row-parallel output x gets a bias,
+ * residual dropout, the residual add, and the next LayerNorm (or RMSNorm).
+ *
+ *   forward   u = x + bias ; keep = Philox(e) >= floor(p * 2^32)
+ *             h = residual + (keep ? u * 1/(1-p) : 0)      (rounded to the I/O type)
+ *             y = Norm(h) * gamma (+ beta)
+ *   backward  dh = Norm'(h)^T (dy * gamma) + dh_out ; dresidual = dh
+ *             dx = keep ? dh / (1-p) : 0 ; dgamma, dbeta, dbias = column sums
+ *
+ * Sources, by page title and section:
+ *  - "Sequence parallel math": rank i owns tokens [i*s/t, (i+1)*s/t) ("The
+ *    one-line idea"); LayerNorm is per token and residual dropout elementwise,
+ *    so a shard computes exactly its slice of the unsharded result ("The move:
+ *    split the LayerNorm/dropout band along the sequence"); the band keeps
+ *    the two LayerNorm inputs, the two dropout masks and the block inputs,
+ *    10*s*b*h replicated under TP and 10*s*b*h/t under SP ("What tensor
+ *    parallelism leaves replicated", "The activation-memory saving, in one
+ *    formula").
+ *  - "Tensor and sequence parallelism -- explained with pictures": a
+ *    sub-block has LayerNorm at its entrance, dropout on its output and a
+ *    residual from its input ("Transformer block"); after the reduce-scatter
+ *    each device applies dropout locally ("Add Sequence parallelism").
+ *  - "SP: Partition Activations Alongside TP": RMSNorm rescales a token from
+ *    its own features and the residual shares the token layout ("Normalize
+ *    and add residuals by token"); after reduce-scatter the SP region adds
+ *    the residual and normalises again ("Connect SP and TP across a layer").
+ *
+ * Readings where the pages are silent: bias is an fp32 [h] vector added
+ * before dropout (NULL = zero); dropout is inverted, scale = fp32(1/(1-p));
+ * the generator is Philox4x32-10 (Salmon et al., SC'11) with key (seed lo,
+ * seed hi) and counter (e/4 lo, e/4 hi, offset lo, offset hi), element e
+ * taking word e mod 4, where e = (shard_index*N + r)*h + c is the element's
+ * index in the FULL [s, b, h] tensor -- a shard draws exactly what the
+ * unsharded run draws; keep iff word >= floor(p*2^32); p == 0 keeps all and
+ * writes no mask; the mask is one byte per element, 1 = keep; h is rounded
+ * to the I/O type (round to nearest even) before the norm reads it;
+ * LayerNorm uses the population variance with eps inside the square root;
+ * RMSNorm is y = gamma*h/sqrt(mean(h^2)+eps) with no beta.
+ *
+ * Conventions for every entry point:
+ *  - N = s_local*b token rows; every per-token tensor is contiguous
+ *    row-major [N, h] (the shard of a sequence-major [s, b, h] tensor).
+ *  - I/O tensors (x, residual, h, y, dy, dh_out, dx, dresidual) have the
+ *    element type desc->io: IEEE binary32, or bfloat16 as raw 16-bit words.
+ *    bias, gamma, beta, mean, rstd, dgamma, dbeta, dbias are always fp32.
+ *  - All pointers are DEVICE pointers (any hipMalloc'd / torch CUDA memory
+ *    of the current device), except desc and the byte-count outputs, which
+ *    are host pointers.  I/O tensors and bias/gamma/beta must be 16-byte
+ *    aligned, mask 8-byte aligned, statistics and gradients 4-byte aligned.
+ *  - h must be a multiple of 8 (bf16) or 4 (fp32), and a row at most 4096
+ *    such 16-byte vectors: h <= 32768 (bf16), h <= 16384 (fp32).
+ *  - Outputs must not overlap inputs or each other.
+ *  - The caller owns every buffer, the workspace included; the library never
+ *    allocates or frees memory and keeps no state between calls.
+ *  - Calls are asynchronous on `stream` (NULL = the null stream): they
+ *    return after the launches and the outputs are valid once the stream
+ *    has reached that point.
+ *  - Errors: every argument is checked on the host before any HIP call; on
+ *    an error nothing is launched and no output is touched.  SPR_ERR_HIP
+ *    means a HIP call failed (the HIP error is consumed); outputs are then
+ *    undefined.
+ */
+#ifndef SP_REGION_H
+#define SP_REGION_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SPR_OK = 0,
+    SPR_ERR_INVALID_ARG = 1,   /* a NULL/misaligned/overlapping pointer or a bad field */
+    SPR_ERR_UNSUPPORTED = 2,   /* valid but not handled: h not a multiple of the vector, h too wide */
+    SPR_ERR_WORKSPACE = 3,     /* workspace missing or smaller than sp_region_bwd_workspace_bytes */
+    SPR_ERR_HIP = 4            /* a HIP launch or query failed */
+} spr_status;
+
+typedef enum { SPR_F32 = 0, SPR_BF16 = 1 } spr_dtype;
+typedef enum { SPR_LAYERNORM = 0, SPR_RMSNORM = 1 } spr_norm;
+
+/* Shard shape and region settings. */
+typedef struct {
+    int64_t  s_local;      /* tokens of this shard along the sequence, s/t (>= 1)   */
+    int64_t  b;            /* batch (>= 1)                                          */
+    int64_t  h;            /* hidden size                                           */
+    int32_t  shard_index;  /* this rank's position in the sequence, 0 <= i < t      */
+    int32_t  t;            /* sequence/tensor-parallel degree (>= 1)                */
+    int32_t  io;           /* spr_dtype of the I/O tensors                          */
+    int32_t  norm;         /* spr_norm                                              */
+    float    p;            /* dropout probability, 0 <= p < 1                       */
+    float    eps;          /* > 0, finite                                           */
+    uint64_t seed;         /* dropout key                                           */
+    uint64_t offset;       /* dropout stream, one per dropout site (e.g. 2*layer+k) */
+} spr_desc;
+
+/* Forward of the region on one shard.
+ *  x        [N,h] io   the reduce-scattered row-parallel output
+ *  bias     [h]  fp32  may be NULL (same as zero)
+ *  residual [N,h] io   the residual stream entering the region
+ *  gamma    [h]  fp32
+ *  beta     [h]  fp32  LayerNorm: required; RMSNorm: must be NULL
+ *  h_out    [N,h] io   residual + dropout(x + bias): the next residual and
+ *                      the norm input kept for the backward
+ *  y_out    [N,h] io   Norm(h): the input of the next tensor-parallel block
+ *  mask_out [N,h] u8   1 = kept; required when p > 0; ignored (may be NULL)
+ *                      when p == 0
+ *  mean_out [N]  fp32  LayerNorm: required; RMSNorm: must be NULL
+ *  rstd_out [N]  fp32  1/sqrt(var + eps) (LayerNorm) or 1/sqrt(mean(h^2)+eps)
+ * h_out and mask_out are bit-exact functions of the inputs; y and the
+ * statistics are computed in fp32. */
+spr_status sp_region_fwd(const spr_desc* desc,
+                         const void* x, const float* bias, const void* residual,
+                         const float* gamma, const float* beta,
+                         void* h_out, void* y_out, uint8_t* mask_out,
+                         float* mean_out, float* rstd_out,
+                         hipStream_t stream);
+
+/* Bytes of device workspace sp_region_bwd needs for this desc (fp32
+ * column partials of dgamma/dbeta/dbias and the kernels' coordination
+ * words).  0 on an invalid desc. */
+size_t sp_region_bwd_workspace_bytes(const spr_desc* desc);
+
+/* Backward of the region on one shard, from the forward's saved tensors.
+ *  dy          [N,h] io   gradient of y
+ *  dh_out      [N,h] io   gradient reaching h from outside the region (the
+ *                         next block's residual branch); may be NULL (zero)
+ *  h, mask, mean, rstd    as written by sp_region_fwd (mask and mean may be
+ *                         NULL when p == 0, resp. for RMSNorm)
+ *  gamma       [h]  fp32
+ *  dx_out      [N,h] io   gradient of x
+ *  dres_out    [N,h] io   gradient of residual (= gradient of h)
+ *  dgamma_out  [h]  fp32  this shard's partial sum over its N rows
+ *  dbeta_out   [h]  fp32  LayerNorm: required; RMSNorm: must be NULL
+ *  dbias_out   [h]  fp32  may be NULL (not computed)
+ *  workspace   device memory of at least sp_region_bwd_workspace_bytes;
+ *              it must be zero-filled before its first use with this
+ *              library, and every call leaves it ready for the next one.
+ *              Concurrent calls must use different workspaces.
+ * The parameter gradients are this shard's partial sums; adding them over
+ * the t shards (a tensor-parallel all-reduce) is the caller's.  The
+ * reductions run in a fixed order: two identical calls give identical bits. */
+spr_status sp_region_bwd(const spr_desc* desc,
+                         const void* dy, const void* dh_out, const void* h,
+                         const uint8_t* mask, const float* mean, const float* rstd,
+                         const float* gamma,
+                         void* dx_out, void* dres_out,
+                         float* dgamma_out, float* dbeta_out, float* dbias_out,
+                         void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
+/* Bytes one forward call keeps (host arithmetic, no device access):
+ *  saved_for_bwd   = h + mask (p > 0) + per-token statistics
+ *  retained_output = y, the next block's input
+ * With bf16 I/O, a one-byte mask and two calls per layer (before attention
+ * and before the MLP) this is 10*s*b*h/t bytes plus the statistics: the
+ * replicated band of "Sequence parallel math" ("What tensor parallelism
+ * leaves replicated"), divided by t. */
+spr_status sp_region_activation_bytes(const spr_desc* desc, uint64_t* saved_for_bwd,
+                                      uint64_t* retained_output);
+
+/* Static description of a status code. */
+const char* sp_region_status_string(spr_status status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SP_REGION_H */

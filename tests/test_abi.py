@@ -1,0 +1,129 @@
+"""The C ABI on the host: the library loads, exports every function that
+include/sp_region.h declares, and rejects invalid calls before any HIP call
+(so these run without a GPU).  No compute call is made here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dropout_region_amd as spr
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sp_region.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(spr.LIB_PATH):
+        pytest.fail("libsp_region.so is not built; run __graft_entry__.build()")
+    return spr.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sp_region_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    assert names == sorted(["sp_region_fwd", "sp_region_bwd", "sp_region_bwd_workspace_bytes",
+                            "sp_region_activation_bytes", "sp_region_status_string"])
+
+
+def test_library_exports_every_declared_function(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings(L):
+    for st in range(5):
+        assert spr.sp_region_status_string(st)
+    assert spr.sp_region_status_string(99) == "unknown status"
+
+
+def _fwd_raw(L, d, ptrs):
+    return L.sp_region_fwd(ctypes.byref(d), *[ctypes.c_void_p(p) for p in ptrs], None)
+
+
+def _good_desc(**kw):
+    base = dict(s_local=4, b=2, h=64, shard_index=0, t=1, io=spr.SPR_BF16,
+                norm=spr.SPR_LAYERNORM, p=0.1, eps=1e-5, seed=0, offset=0)
+    base.update(kw)
+    return spr.Desc(**base).c()
+
+
+# Fake, never-dereferenced device addresses: each call below must fail in the
+# host checks, before the library touches HIP.
+A = 0x7f0000000000
+FWD_OK = [A, A + 0x100000, A + 0x200000, A + 0x300000, A + 0x310000, A + 0x400000,
+          A + 0x500000, A + 0x600000, A + 0x700000, A + 0x710000]
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("p", 1.0, spr.SPR_ERR_INVALID_ARG), ("p", -0.5, spr.SPR_ERR_INVALID_ARG),
+    ("p", float("nan"), spr.SPR_ERR_INVALID_ARG), ("eps", 0.0, spr.SPR_ERR_INVALID_ARG),
+    ("eps", float("inf"), spr.SPR_ERR_INVALID_ARG), ("t", 0, spr.SPR_ERR_INVALID_ARG),
+    ("shard_index", 1, spr.SPR_ERR_INVALID_ARG), ("shard_index", -1, spr.SPR_ERR_INVALID_ARG),
+    ("h", 0, spr.SPR_ERR_INVALID_ARG), ("s_local", 0, spr.SPR_ERR_INVALID_ARG),
+    ("io", 5, spr.SPR_ERR_INVALID_ARG), ("norm", 2, spr.SPR_ERR_INVALID_ARG),
+    ("h", 60, spr.SPR_ERR_UNSUPPORTED), ("h", 32776, spr.SPR_ERR_UNSUPPORTED),
+])
+def test_fwd_rejects_bad_desc(L, field, value, status):
+    d = _good_desc(**{field: value})
+    assert _fwd_raw(L, d, FWD_OK) == status
+
+
+def test_fwd_pointer_rules(L):
+    d = _good_desc()
+    bad = list(FWD_OK)
+    bad[0] = 0                                   # x missing
+    assert _fwd_raw(L, d, bad) == spr.SPR_ERR_INVALID_ARG
+    bad = list(FWD_OK)
+    bad[0] = A + 8                               # x misaligned
+    assert _fwd_raw(L, d, bad) == spr.SPR_ERR_INVALID_ARG
+    bad = list(FWD_OK)
+    bad[7] = 0                                   # mask missing with p > 0
+    assert _fwd_raw(L, d, bad) == spr.SPR_ERR_INVALID_ARG
+    bad = list(FWD_OK)
+    bad[4] = 0                                   # beta missing for LayerNorm
+    assert _fwd_raw(L, d, bad) == spr.SPR_ERR_INVALID_ARG
+    rms = _good_desc(norm=spr.SPR_RMSNORM)
+    assert _fwd_raw(L, rms, FWD_OK) == spr.SPR_ERR_INVALID_ARG   # beta given for RMSNorm
+    bad = list(FWD_OK)
+    bad[5] = FWD_OK[0] + 16                      # h_out overlaps x
+    assert _fwd_raw(L, d, bad) == spr.SPR_ERR_INVALID_ARG
+    bad = list(FWD_OK)
+    bad[6] = FWD_OK[5]                           # y_out aliases h_out
+    assert _fwd_raw(L, d, bad) == spr.SPR_ERR_INVALID_ARG
+
+
+def test_bwd_workspace_rules(L):
+    d = _good_desc()
+    need = L.sp_region_bwd_workspace_bytes(ctypes.byref(d))
+    assert need > 0 and need % 256 == 0
+    assert L.sp_region_bwd_workspace_bytes(ctypes.byref(_good_desc(p=2.0))) == 0
+    ptrs = [A + i * 0x100000 for i in range(12)]
+    ptrs[1] = 0                                  # no dh_out
+    call = lambda ws, n: L.sp_region_bwd(ctypes.byref(d), *[ctypes.c_void_p(p) for p in ptrs],
+                                         ctypes.c_void_p(ws), ctypes.c_size_t(n), None)
+    assert call(0, need) == spr.SPR_ERR_WORKSPACE
+    assert call(A + 0x4000000, need - 1) == spr.SPR_ERR_WORKSPACE
+    d_rms = _good_desc(norm=spr.SPR_RMSNORM)     # dbeta given for RMSNorm
+    assert L.sp_region_bwd(ctypes.byref(d_rms), *[ctypes.c_void_p(p) for p in ptrs],
+                           ctypes.c_void_p(A + 0x4000000), ctypes.c_size_t(need),
+                           None) == spr.SPR_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("io,norm,p", [(spr.SPR_BF16, spr.SPR_LAYERNORM, 0.1),
+                                       (spr.SPR_F32, spr.SPR_LAYERNORM, 0.1),
+                                       (spr.SPR_BF16, spr.SPR_RMSNORM, 0.0),
+                                       (spr.SPR_F32, spr.SPR_RMSNORM, 0.3)])
+def test_activation_bytes_agree_with_oracle(L, olib, io, norm, p):
+    for (s_local, b, h) in [(256, 4, 6144), (256, 8, 12288), (4096, 1, 8192), (2048, 4, 25600),
+                            (64, 2, 256)]:
+        d = spr.Desc(s_local=s_local, b=b, h=h, io=io, norm=norm, p=p)
+        od = oracle.Desc(s_local=s_local, b=b, h=h, io=io, norm=norm, p=p)
+        assert spr.sp_region_activation_bytes(d) == oracle.activation_bytes(od, L=olib)

@@ -1,0 +1,238 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Masks and h must be bit-exact; y, the statistics and the gradients must meet
+the tolerances in tests/parity.py.  Every backward check feeds both sides the
+oracle's saved tensors (so the backward is judged alone), runs the GPU call
+twice into the same buffers (results must be bit-identical), and also runs
+the GPU backward from the GPU forward's own saved tensors (the chain).
+"""
+import zlib
+
+import numpy as np
+import pytest
+
+import dropout_region_amd as spr
+import oracle
+from sp_inputs import WORKLOADS, make_inputs
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+F32, BF16, LN, RMS = spr.SPR_F32, spr.SPR_BF16, spr.SPR_LAYERNORM, spr.SPR_RMSNORM
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    spr.lib()                            # raises if the HIP library is missing
+
+
+def descs(**kw):
+    return spr.Desc(**kw), oracle.Desc(**kw)
+
+
+def run_case(name, kw, seed=0, with_bias=True, with_dh_out=False, want_dbias=True):
+    d, od = descs(**kw)
+    _say(f"[case] {name}: {kw} bias={with_bias} dh_out={with_dh_out} dbias={want_dbias}")
+    inp = make_inputs(d.rows, d.h, d.io, seed=seed, dh_out=with_dh_out)
+    want = P.oracle_fwd(od, inp, with_bias)
+    got = P.gpu_fwd(d, inp, with_bias)
+    P.check_fwd(got, want, d.io)
+    wb = P.oracle_bwd(od, inp, want, with_dh_out, want_dbias)
+    gb = P.gpu_bwd(d, inp, want, with_dh_out, want_dbias, repeat=2)
+    P.check_bwd(gb, wb, d.io)
+    gc = P.gpu_bwd(d, inp, got, with_dh_out, want_dbias)
+    P.check_bwd(gc, wb, d.io)
+    return inp, got, gb
+
+
+def base(**kw):
+    b = dict(s_local=8, b=2, h=256, shard_index=0, t=1, io=BF16, norm=LN, p=0.1, eps=1e-5,
+             seed=0, offset=0)
+    b.update(kw)
+    return b
+
+
+SMALL = {
+    "fp32_ln_h256_shard1of2": base(s_local=64, h=256, shard_index=1, t=2, io=F32),
+    "bf16_ln_h6144_shard5of8": base(s_local=10, b=3, h=6144, shard_index=5, t=8),
+    "bf16_rms_h8192_p0": base(s_local=17, b=1, h=8192, norm=RMS, p=0.0, eps=1e-6),
+    "bf16_rms_h8192_p0.1": base(s_local=17, b=1, h=8192, norm=RMS, p=0.1, eps=1e-6),
+    "bf16_ln_h12288": base(s_local=3, b=3, h=12288, shard_index=2, t=8),
+    "bf16_ln_h25600": base(s_local=5, b=1, h=25600, shard_index=7, t=8),
+    "bf16_ln_h1000_ragged_wave_rows": base(s_local=37, b=1, h=1000),
+    "bf16_ln_h2056_ragged_wg_row": base(s_local=7, b=2, h=2056),
+    "fp32_ln_h260_ragged": base(s_local=13, b=3, h=260, io=F32),
+    "fp32_rms_h3076_ragged": base(s_local=6, b=2, h=3076, io=F32, norm=RMS, p=0.3),
+    "bf16_ln_h8_single_vector": base(s_local=5, b=1, h=8, p=0.5),
+    "fp32_ln_h4_single_vector": base(s_local=9, b=1, h=4, io=F32, p=0.5),
+    "bf16_ln_h32768_widest": base(s_local=2, b=1, h=32768),
+    "fp32_ln_h16384_widest": base(s_local=2, b=1, h=16384, io=F32),
+    "bf16_ln_one_row": base(s_local=1, b=1, h=6144),
+    "bf16_ln_h6144_1003_rows": base(s_local=1003, b=1, h=6144),
+    "fp32_ln_h256_1001_rows": base(s_local=1001, b=1, h=256, io=F32),
+    "bf16_ln_high_counter_words": base(s_local=2, b=1, h=32768, shard_index=2**20 - 1,
+                                       t=2**20, seed=2**64 - 1, offset=2**63 + 5),
+    "bf16_ln_p0.9": base(s_local=4, b=2, h=6144, p=0.9),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_small_shapes(name):
+    run_case(name, SMALL[name], seed=zlib.crc32(name.encode()) % 1000, with_dh_out=True)
+
+
+@pytest.mark.parametrize("with_bias,with_dh_out,want_dbias", [(False, False, True),
+                                                              (True, False, False),
+                                                              (False, True, False)])
+@pytest.mark.parametrize("io,norm", [(BF16, LN), (F32, RMS)])
+def test_optional_arguments(with_bias, with_dh_out, want_dbias, io, norm):
+    kw = base(s_local=6, b=2, h=6144 if io == BF16 else 1024, io=io, norm=norm)
+    run_case(f"optional io={io} norm={norm}", kw, seed=3, with_bias=with_bias,
+             with_dh_out=with_dh_out, want_dbias=want_dbias)
+
+
+@pytest.mark.parametrize("io,h,t", [(F32, 256, 2), (BF16, 6144, 4), (BF16, 25600, 2)])
+def test_shard_invariance(io, h, t):
+    """Concatenating the t shard results equals the unsharded (t = 1) run:
+    bit-exact for every per-token output, and the parameter gradients summed
+    over shards match within tolerance."""
+    s, b = 16, 2
+    full, _ = descs(**base(s_local=s, b=b, h=h, io=io, t=1, offset=3))
+    _say(f"[case] shard invariance io={io} h={h} t={t}")
+    inp = make_inputs(full.rows, h, io, seed=11, dh_out=True)
+    ref = P.gpu_fwd(full, inp)
+    refb = P.gpu_bwd(full, inp, ref, with_dh_out=True)
+    N = full.rows // t
+    acc = {k: np.zeros(h) for k in ("dgamma", "dbeta", "dbias")}
+    for i in range(t):
+        d, _ = descs(**base(s_local=s // t, b=b, h=h, io=io, shard_index=i, t=t, offset=3))
+        sl = slice(i * N * h, (i + 1) * N * h)
+        si = {k: (v[sl] if v is not None and v.size == full.rows * h else v) for k, v in inp.items()}
+        o = P.gpu_fwd(d, si)
+        for k in ("h", "y", "mask"):
+            P.exact(f"{k} shard {i}", o[k], ref[k][sl])
+        for k in ("mean", "rstd"):
+            P.exact(f"{k} shard {i}", o[k], ref[k][i * N:(i + 1) * N])
+        g = P.gpu_bwd(d, si, o, with_dh_out=True)
+        for k in ("dx", "dres"):
+            P.exact(f"{k} shard {i}", g[k], refb[k][sl])
+        for k in acc:
+            acc[k] += g[k]
+    for k in acc:
+        P.param_grad_close(f"sum of shard {k}", acc[k], refb[k])
+
+
+def test_workspace_and_argument_errors_leave_outputs_untouched():
+    import torch
+    d, _ = descs(**base(s_local=4, b=2, h=6144))
+    inp = make_inputs(d.rows, d.h, d.io, seed=1)
+    dev = "cuda:0"
+    x, res = P.to_device(inp["x"], BF16), P.to_device(inp["residual"], BF16)
+    g, bt = P.to_device(inp["gamma"]), P.to_device(inp["beta"])
+    o = spr.alloc_fwd_outputs(d, dev)
+    for v in o.values():
+        v.view(torch.uint8).fill_(0xA5)
+    bad = spr.Desc(**dict(base(s_local=4, b=2, h=6144), p=1.5))
+    with pytest.raises(spr.SprError) as e:
+        spr.sp_region_fwd(bad, x, None, res, g, bt, o["h"], o["y"], o["mask"], o["mean"], o["rstd"])
+    assert e.value.status == spr.SPR_ERR_INVALID_ARG
+    torch.cuda.synchronize()
+    for v in o.values():
+        assert bool((v.view(torch.uint8) == 0xA5).all())
+    spr.sp_region_fwd(d, x, None, res, g, bt, o["h"], o["y"], o["mask"], o["mean"], o["rstd"])
+    ob = spr.alloc_bwd_outputs(d, dev)
+    small = ob["workspace"][:-256] if ob["workspace"].numel() > 256 else ob["workspace"][:0]
+    with pytest.raises(spr.SprError) as e:
+        spr.sp_region_bwd(d, x, None, o["h"], o["mask"], o["mean"], o["rstd"], g, ob["dx"],
+                          ob["dres"], ob["dgamma"], ob["dbeta"], ob["dbias"], small)
+    assert e.value.status == spr.SPR_ERR_WORKSPACE
+
+
+def test_outputs_stay_inside_their_buffers():
+    """Every output is a view into a larger buffer whose guard bands hold a
+    pattern; after fwd and bwd the guards are unchanged."""
+    import torch
+    G = 256                                   # guard elements (keeps 16-byte alignment)
+    for kw in (base(s_local=7, b=3, h=2056), base(s_local=9, b=1, h=260, io=F32),
+               base(s_local=3, b=1, h=25600)):
+        d, _ = descs(**kw)
+        _say(f"[case] guards {kw}")
+        inp = make_inputs(d.rows, d.h, d.io, seed=2, dh_out=True)
+        dev = "cuda:0"
+
+        def guarded(n, dtype):
+            full = torch.empty(n + 2 * G, dtype=dtype, device=dev)
+            full.view(torch.uint8).fill_(0x5A)
+            return full, full[G:G + n]
+
+        io = torch.bfloat16 if d.io == BF16 else torch.float32
+        N, H = d.rows, d.h
+        bufs = {k: guarded(n, dt) for k, (n, dt) in {
+            "h": (N * H, io), "y": (N * H, io), "mask": (N * H, torch.uint8),
+            "mean": (N, torch.float32), "rstd": (N, torch.float32), "dx": (N * H, io),
+            "dres": (N * H, io), "dgamma": (H, torch.float32), "dbeta": (H, torch.float32),
+            "dbias": (H, torch.float32),
+            "ws": (spr.sp_region_bwd_workspace_bytes(d) // 4, torch.float32)}.items()}
+        v = {k: b[1] for k, b in bufs.items()}
+        v["ws"].zero_()
+        spr.sp_region_fwd(d, P.to_device(inp["x"], d.io), P.to_device(inp["bias"]),
+                          P.to_device(inp["residual"], d.io), P.to_device(inp["gamma"]),
+                          P.to_device(inp["beta"]), v["h"], v["y"], v["mask"], v["mean"], v["rstd"])
+        spr.sp_region_bwd(d, P.to_device(inp["dy"], d.io), P.to_device(inp["dh_out"], d.io),
+                          v["h"], v["mask"], v["mean"], v["rstd"], P.to_device(inp["gamma"]),
+                          v["dx"], v["dres"], v["dgamma"], v["dbeta"], v["dbias"], v["ws"])
+        torch.cuda.synchronize()
+        for k, (full, _) in bufs.items():
+            raw = full.view(torch.uint8)
+            gb = G * full.element_size()
+            assert bool((raw[:gb] == 0x5A).all()) and bool((raw[-gb:] == 0x5A).all()), k
+
+
+# ------------------------------------------------------------------ full size
+def _full_kw(w, shard_index=0, offset=0):
+    return dict(s_local=w.s_local, b=w.b, h=w.h, shard_index=shard_index, t=w.t, io=w.io,
+                norm=w.norm, p=w.p, eps=w.eps, seed=w.seed, offset=offset)
+
+
+@pytest.mark.parametrize("name", ["22b_h6144_t8", "longseq_rms_h8192_t8_p0.1",
+                                  "longseq_rms_h8192_t8_p0", "1t_h25600_t8", "1t_h25600_t4",
+                                  "1t_h25600_t2", "1t_h25600_t1"])
+def test_full_size_workload(name):
+    """The workloads at their real shard shapes, in the launch configuration
+    the benchmark times; every element is compared."""
+    w = WORKLOADS[name]
+    run_case(name, _full_kw(w), seed=w.seed, with_dh_out=(w.norm == RMS))
+
+
+def test_full_size_175b_layer_two_calls():
+    """175B-class layer: the pre-attention and pre-MLP region calls chained
+    as in a layer (call B's residual is call A's h; call A's backward gets
+    call B's dresidual as dh_out), offsets 0 and 1 for the two dropout sites."""
+    w = WORKLOADS["175b_h12288_t8"]
+    dA, odA = descs(**_full_kw(w, offset=0))
+    dB, odB = descs(**_full_kw(w, offset=1))
+    _say(f"[case] 175b layer: {_full_kw(w)}")
+    inA = make_inputs(dA.rows, dA.h, dA.io, seed=0)
+    inB = make_inputs(dB.rows, dB.h, dB.io, seed=1)
+    # forward: A then B, B's residual = A's h
+    wA = P.oracle_fwd(odA, inA)
+    gA = P.gpu_fwd(dA, inA)
+    P.check_fwd(gA, wA, dA.io)
+    inB_o = dict(inB, residual=wA["h"])
+    wB = P.oracle_fwd(odB, inB_o)
+    gB = P.gpu_fwd(dB, dict(inB, residual=gA["h"]))
+    P.check_fwd(gB, wB, dB.io)
+    # backward: B then A, A's dh_out = B's dresidual
+    wbB = P.oracle_bwd(odB, inB_o, wB)
+    gbB = P.gpu_bwd(dB, inB_o, wB)
+    P.check_bwd(gbB, wbB, dB.io)
+    inA_b = dict(inA, dh_out=wbB["dres"])
+    wbA = P.oracle_bwd(odA, inA_b, wA, with_dh_out=True)
+    gbA = P.gpu_bwd(dA, inA_b, wA, with_dh_out=True)
+    P.check_bwd(gbA, wbA, dA.io)
