@@ -22,10 +22,22 @@
 
 namespace spr {
 
+// The saved tensors of one row as loaded (raw words; decoded when used).
+template <int VPT, int MW>
+struct RowIn {
+    uint4 h[VPT], dy[VPT], dho[VPT];
+    uint32_t mask[VPT][MW];
+    float mu, rs;
+};
+
 template <typename IO, int NORM, bool DROP, int VPT, bool WAVE_ROWS, int LB>
 __global__ void __launch_bounds__(LB) sp_region_bwd_rows_kernel(BwdArgs a) {
+    // Prefetching the next row doubles the row's registers; wide rows
+    // (more than two vectors per thread) load each row when they reach it.
+    constexpr bool PREFETCH = VPT <= 2;
     using V = Vec<IO>;
     constexpr int E = V::N;
+    constexpr int MW = E / 4;                 // mask words per vector
     __shared__ float red[2][32];
 
     int tid, tpr, nwaves;
@@ -42,49 +54,71 @@ __global__ void __launch_bounds__(LB) sp_region_bwd_rows_kernel(BwdArgs a) {
         team = blockIdx.x;
     }
 
-    float acc_g[VPT][E], acc_b[VPT][E], acc_x[VPT][E];
+    // Idle vector slots of a ragged row re-read the row's last vector; their
+    // results are masked out of every sum and never stored.
+    int vc[VPT];
+    bool ok[VPT];
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
+        const int vec = k * tpr + tid;
+        ok[k] = vec < a.nvec;
+        vc[k] = ok[k] ? vec : a.nvec - 1;
+    }
+
+    float gam[VPT][E], acc_g[VPT][E], acc_b[VPT][E], acc_x[VPT][E];
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+        load_params<E>(a.gamma + (int64_t)vc[k] * E, gam[k]);
 #pragma unroll
         for (int j = 0; j < E; ++j) acc_g[k][j] = acc_b[k][j] = acc_x[k][j] = 0.0f;
     }
 
-    int slot = 0;
-    // The trip count is uniform over the team (and over the workgroup when
-    // the workgroup is the team), so every thread meets every barrier.
-    for (int64_t row = team; row < a.rows; row += a.teams) {
+    auto load_row = [&](int64_t row, RowIn<VPT, MW>& in) {
         const int64_t rbase = row * a.hidden;
-        V hv[VPT], dyv[VPT];
-        uint32_t kb[VPT];
 #pragma unroll
         for (int k = 0; k < VPT; ++k) {
-            const int vec = k * tpr + tid;
-            kb[k] = 0xffu;
-            if (vec < a.nvec) {
-                const int64_t off = rbase + (int64_t)vec * E;
-                hv[k].load(static_cast<const IO*>(a.h) + off);
-                dyv[k].load(static_cast<const IO*>(a.dy) + off);
-                if (DROP) kb[k] = MaskBytes<E>::load(a.mask + off);
-            } else {
+            const int64_t off = rbase + (int64_t)vc[k] * E;
+            in.h[k] = load_stream(static_cast<const IO*>(a.h) + off);
+            in.dy[k] = load_stream(static_cast<const IO*>(a.dy) + off);
+            if (DROP) {
 #pragma unroll
-                for (int j = 0; j < E; ++j) hv[k].v[j] = dyv[k].v[j] = 0.0f;
+                for (int w = 0; w < MW; ++w)
+                    in.mask[k][w] = __builtin_nontemporal_load(
+                        reinterpret_cast<const uint32_t*>(a.mask + off) + w);
             }
+            if (a.dh_out) in.dho[k] = load_stream(static_cast<const IO*>(a.dh_out) + off);
         }
-        const float mu = (NORM == SPR_LAYERNORM) ? a.mean[row] : 0.0f;
-        const float rs = a.rstd[row];
+        in.mu = (NORM == SPR_LAYERNORM) ? a.mean[row] : 0.0f;
+        in.rs = a.rstd[row];
+    };
 
-        // g and xhat are recomputed in the second pass rather than kept
+    // Rows team, team + teams, ...: the trip count is uniform over the team
+    // (the workgroup, when the workgroup is the team), so every thread meets
+    // every barrier.  The next row's loads are issued before this row's
+    // reduction, so they are in flight while it is computed and stored.
+    RowIn<VPT, MW> cur, nxt;
+    int64_t row = team;
+    if (PREFETCH && row < a.rows) load_row(row, cur);
+    int slot = 0;
+    for (; row < a.rows; row += a.teams) {
+        const int64_t next = row + a.teams;
+        if (PREFETCH) {
+            if (next < a.rows) load_row(next, nxt);
+        } else {
+            load_row(row, cur);
+        }
+
+        V hv[VPT], dyv[VPT];
         float s1 = 0.0f, s2 = 0.0f;
 #pragma unroll
         for (int k = 0; k < VPT; ++k) {
-            const int vec = k * tpr + tid;
-            if (vec < a.nvec) {
-                float gam[E];
-                load_params<E>(a.gamma + (int64_t)vec * E, gam);
+            hv[k].set(cur.h[k]);
+            dyv[k].set(cur.dy[k]);
 #pragma unroll
-                for (int j = 0; j < E; ++j) {
-                    const float xh = (hv[k].v[j] - mu) * rs;
-                    const float g = dyv[k].v[j] * gam[j];
+            for (int j = 0; j < E; ++j) {
+                const float xh = (hv[k].v[j] - cur.mu) * cur.rs;
+                const float g = dyv[k].v[j] * gam[k][j];
+                if (ok[k]) {
                     s1 += g;
                     s2 += g * xh;
                 }
@@ -94,42 +128,46 @@ __global__ void __launch_bounds__(LB) sp_region_bwd_rows_kernel(BwdArgs a) {
         slot ^= 1;
         const float mg = s1 * a.inv_h, mgx = s2 * a.inv_h;
 
+        const int64_t rbase = row * a.hidden;
 #pragma unroll
         for (int k = 0; k < VPT; ++k) {
-            const int vec = k * tpr + tid;
-            if (vec < a.nvec) {
-                const int64_t off = rbase + (int64_t)vec * E;
-                V dho;
-                if (a.dh_out) dho.load(static_cast<const IO*>(a.dh_out) + off);
-                float gam[E];
-                load_params<E>(a.gamma + (int64_t)vec * E, gam);
-                V dres, dx;
+            V dho, dres, dx;
+            if (a.dh_out) dho.set(cur.dho[k]);
+            uint32_t kb = 0xffu;
+            if (DROP) {
+                kb = MaskBytes<4>::from_word(cur.mask[k][0]);
+                if (MW == 2) kb |= MaskBytes<4>::from_word(cur.mask[k][MW - 1]) << 4;
+            }
 #pragma unroll
-                for (int j = 0; j < E; ++j) {
-                    const float xh = (hv[k].v[j] - mu) * rs;
-                    const float g = dyv[k].v[j] * gam[j];
-                    float dh = (NORM == SPR_LAYERNORM) ? rs * (g - mg - xh * mgx)
-                                                       : rs * (g - xh * mgx);
-                    if (a.dh_out) dh += dho.v[j];
-                    const float dxu = DROP ? (((kb[k] >> j) & 1u) ? dh * a.scale : 0.0f) : dh;
-                    dres.v[j] = dh;
-                    dx.v[j] = dxu;
+            for (int j = 0; j < E; ++j) {
+                const float xh = (hv[k].v[j] - cur.mu) * cur.rs;
+                const float g = dyv[k].v[j] * gam[k][j];
+                float dh = (NORM == SPR_LAYERNORM) ? cur.rs * (g - mg - xh * mgx)
+                                                   : cur.rs * (g - xh * mgx);
+                if (a.dh_out) dh += dho.v[j];
+                const float dxu = DROP ? (((kb >> j) & 1u) ? dh * a.scale : 0.0f) : dh;
+                dres.v[j] = dh;
+                dx.v[j] = dxu;
+                if (ok[k]) {
                     acc_g[k][j] += dyv[k].v[j] * xh;
                     acc_b[k][j] += dyv[k].v[j];
                     acc_x[k][j] += dxu;
                 }
+            }
+            if (ok[k]) {
+                const int64_t off = rbase + (int64_t)vc[k] * E;
                 dres.store(static_cast<IO*>(a.dres_out) + off);
                 dx.store(static_cast<IO*>(a.dx_out) + off);
             }
         }
+        if (PREFETCH) cur = nxt;
     }
 
     float* part = a.partials + team * 3 * a.hidden;
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
-        const int vec = k * tpr + tid;
-        if (vec < a.nvec) {
-            const int64_t c = (int64_t)vec * E;
+        if (ok[k]) {
+            const int64_t c = (int64_t)vc[k] * E;
 #pragma unroll
             for (int j = 0; j < E; j += 4) {
                 *reinterpret_cast<float4*>(part + c + j) =
@@ -143,26 +181,47 @@ __global__ void __launch_bounds__(LB) sp_region_bwd_rows_kernel(BwdArgs a) {
     }
 }
 
-// out_k[c] = sum over teams t (in order) of partials[t][k][c], k = dgamma,
-// dbeta, dbias; an output whose pointer is NULL is skipped.
+// out_k[c] = sum over teams t = 0, 1, ... of partials[t][k][c] (k = dgamma,
+// dbeta, dbias over the flat index j = k*h + c).  A workgroup owns 64
+// consecutive j (16 lanes x float4) and splits the teams over 16 lane
+// groups: group q adds teams q, q+16, ... in order, then the 16 group sums
+// are added in group order.  Fixed order throughout: the result does not
+// depend on scheduling.  An output whose pointer is NULL is skipped.
+constexpr int kFinCols = 64, kFinGroups = 16;
 __global__ void __launch_bounds__(256) sp_region_bwd_finalize_kernel(BwdArgs a) {
-    const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (j >= 3 * a.hidden) return;
-    const int k = (int)(j / a.hidden);
-    const int64_t c = j - (int64_t)k * a.hidden;
-    float* out = k == 0 ? a.dgamma_out : (k == 1 ? a.dbeta_out : a.dbias_out);
-    if (!out) return;
-    const float* p = a.partials + (int64_t)k * a.hidden + c;
-    float s = 0.0f;
-    for (int t = 0; t < a.teams; ++t) s += p[(int64_t)t * 3 * a.hidden];
-    out[c] = s;
+    __shared__ float4 part[kFinGroups][kFinCols / 4];
+    const int lane = threadIdx.x % (kFinCols / 4), q = threadIdx.x / (kFinCols / 4);
+    const int64_t j = (int64_t)blockIdx.x * kFinCols + lane * 4;
+    const int64_t n3 = 3 * a.hidden;
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (j < n3) {
+        const float* p = a.partials + j;
+        for (int t = q; t < a.teams; t += kFinGroups) {
+            const float4 v = *reinterpret_cast<const float4*>(p + (int64_t)t * n3);
+            s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+        }
+    }
+    part[q][lane] = s;
+    __syncthreads();
+    if (q == 0 && j < n3) {
+        float4 t = part[0][lane];
+        for (int g = 1; g < kFinGroups; ++g) {
+            const float4 v = part[g][lane];
+            t.x += v.x; t.y += v.y; t.z += v.z; t.w += v.w;
+        }
+        const int k = (int)(j / a.hidden);
+        const int64_t c = j - (int64_t)k * a.hidden;
+        float* out = k == 0 ? a.dgamma_out : (k == 1 ? a.dbeta_out : a.dbias_out);
+        if (out) *reinterpret_cast<float4*>(out + c) = t;
+    }
 }
 
-// Teams: enough to cover the chip a couple of times over while keeping the
-// partial rows (3*h fp32 each, written once and read once) few.
+// Teams: one workgroup per CU (fewer workgroups cannot draw the full HBM
+// bandwidth) and no more, since each team writes one partial row of 3*h fp32
+// that the finalize reads back.
 int64_t bwd_teams(const spr_desc& d, const RowPlan& p) {
     const int64_t rows = d.s_local * d.b;
-    const int64_t cap = 256;
+    const int64_t cap = 256 * (int64_t)p.rpw;       // one workgroup per CU
     const int64_t want = rows < cap ? rows : cap;
     return ((want + p.rpw - 1) / p.rpw) * p.rpw;
 }
@@ -174,25 +233,25 @@ static hipError_t bwd_by_vpt(const RowPlan& p, const BwdArgs& a, hipStream_t s) 
     case V:                                                                                      \
         hipLaunchKernelGGL((sp_region_bwd_rows_kernel<IO, NORM, DROP, V, WR, L>), g, b, 0, s, a); \
         break;
-    if (WR) {
+    if constexpr (WR) {
         switch (p.vpt) {
             SPR_BWD_CASE(1, 256) SPR_BWD_CASE(2, 256) SPR_BWD_CASE(3, 256) SPR_BWD_CASE(4, 256)
             default: return hipErrorInvalidValue;
         }
     } else {
-        // must match kWgCombos
+        // must match kBwdCombos
         switch (p.vpt) {
-            SPR_BWD_CASE(1, 1024) SPR_BWD_CASE(2, 1024) SPR_BWD_CASE(3, 1024)
-            SPR_BWD_CASE(4, 1024) SPR_BWD_CASE(5, 768) SPR_BWD_CASE(6, 768) SPR_BWD_CASE(8, 512)
+            SPR_BWD_CASE(1, 1024) SPR_BWD_CASE(2, 768) SPR_BWD_CASE(3, 512)
+            SPR_BWD_CASE(4, 512) SPR_BWD_CASE(5, 640) SPR_BWD_CASE(6, 512) SPR_BWD_CASE(8, 512)
             default: return hipErrorInvalidValue;
         }
     }
 #undef SPR_BWD_CASE
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t n = 3 * a.hidden;
-    hipLaunchKernelGGL(sp_region_bwd_finalize_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256),
-                       0, s, a);
+    const int64_t n3 = 3 * a.hidden;
+    hipLaunchKernelGGL(sp_region_bwd_finalize_kernel, dim3((unsigned)((n3 + kFinCols - 1) / kFinCols)),
+                       dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

@@ -17,17 +17,23 @@ struct Philox4 {
     uint32_t w0, w1, w2, w3;
 };
 
+// Three-input XOR in one CDNA4 instruction (v_bitop3_b32, truth table 0x96).
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+    return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+}
+
 // One Philox4x32-10 block.  The key schedule adds the Weyl constants between
 // rounds; c2/c3/k0/k1 are wave-uniform here, so the compiler keeps their
-// first-round work on the scalar unit.
+// first-round work on the scalar unit.  Per round: two 32x32->64 products
+// (v_mad_u64_u32) and two three-input XORs.
 __device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2,
                                                  uint32_t c3, uint32_t k0, uint32_t k1) {
 #pragma unroll
     for (int round = 0; round < 10; ++round) {
         const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
         const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
-        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
-        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        const uint32_t n0 = xor3((uint32_t)(p1 >> 32), c1, k0);
+        const uint32_t n2 = xor3((uint32_t)(p0 >> 32), c3, k1);
         c1 = (uint32_t)p1;
         c3 = (uint32_t)p0;
         c0 = n0;
@@ -38,14 +44,23 @@ __device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint3
     return {c0, c1, c2, c3};
 }
 
-// Keep bits of the 4 consecutive elements 4*blk .. 4*blk+3 of the full
-// tensor: bit j set iff word j >= thr.
-__device__ __forceinline__ uint32_t keep4(uint64_t blk, uint32_t off_lo, uint32_t off_hi,
-                                         uint32_t key_lo, uint32_t key_hi, uint32_t thr) {
+// Keep decisions of the 4 consecutive elements 4*blk .. 4*blk+3 of the full
+// tensor: element 4*blk + j is kept iff word j >= thr.
+__device__ __forceinline__ void keep4(uint64_t blk, uint32_t off_lo, uint32_t off_hi,
+                                      uint32_t key_lo, uint32_t key_hi, uint32_t thr,
+                                      bool* keep) {
     const Philox4 r = philox4x32_10((uint32_t)blk, (uint32_t)(blk >> 32), off_lo, off_hi,
                                     key_lo, key_hi);
-    return (uint32_t)(r.w0 >= thr) | ((uint32_t)(r.w1 >= thr) << 1) |
-           ((uint32_t)(r.w2 >= thr) << 2) | ((uint32_t)(r.w3 >= thr) << 3);
+    keep[0] = r.w0 >= thr;
+    keep[1] = r.w1 >= thr;
+    keep[2] = r.w2 >= thr;
+    keep[3] = r.w3 >= thr;
+}
+
+// Mask word of 4 keep decisions: byte j is 1 when element j is kept.
+__device__ __forceinline__ uint32_t mask_word(const bool* keep) {
+    return (keep[0] ? 1u : 0u) | (keep[1] ? 1u << 8 : 0u) | (keep[2] ? 1u << 16 : 0u) |
+           (keep[3] ? 1u << 24 : 0u);
 }
 
 // ------------------------------------------------------------------ h
@@ -73,19 +88,35 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 // ------------------------------------------------------------------ vectors
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// Streaming 16-byte accesses: each byte of x, residual, h, y, dy, dx, dres is
+// touched once per kernel, so they carry the nontemporal hint.
+__device__ __forceinline__ uint4 load_stream(const void* p) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store_stream(void* p, uint4 q) {
+    const u32x4_t v = {q.x, q.y, q.z, q.w};
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(p));
+}
+
 // One 16-byte vector of the I/O type, widened to fp32.
 template <typename IO> struct Vec;
 
 template <> struct Vec<float> {
     static constexpr int N = 4;
     float v[4];
-    __device__ __forceinline__ void load(const void* p) {
-        const float4 q = *reinterpret_cast<const float4*>(p);
-        v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+    __device__ __forceinline__ void set(uint4 q) {
+        v[0] = __uint_as_float(q.x); v[1] = __uint_as_float(q.y);
+        v[2] = __uint_as_float(q.z); v[3] = __uint_as_float(q.w);
     }
-    __device__ __forceinline__ void store(void* p) const {
-        *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    __device__ __forceinline__ uint4 get() const {
+        return make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                          __float_as_uint(v[3]));
     }
+    __device__ __forceinline__ void load(const void* p) { set(load_stream(p)); }
+    __device__ __forceinline__ void store(void* p) const { store_stream(p, get()); }
     // value as stored in the I/O type (identity for fp32)
     __device__ __forceinline__ static float round_io(float f) { return f; }
 };
@@ -93,21 +124,18 @@ template <> struct Vec<float> {
 template <> struct Vec<__bf16> {
     static constexpr int N = 8;
     float v[8];
-    __device__ __forceinline__ void load(const void* p) {
-        const uint4 q = *reinterpret_cast<const uint4*>(p);
+    __device__ __forceinline__ void set(uint4 q) {
         v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x);
         v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
         v[4] = bf16_lo(q.z); v[5] = bf16_hi(q.z);
         v[6] = bf16_lo(q.w); v[7] = bf16_hi(q.w);
     }
-    __device__ __forceinline__ void store(void* p) const {
-        uint4 q;
-        q.x = pack_bf16x2(v[0], v[1]);
-        q.y = pack_bf16x2(v[2], v[3]);
-        q.z = pack_bf16x2(v[4], v[5]);
-        q.w = pack_bf16x2(v[6], v[7]);
-        *reinterpret_cast<uint4*>(p) = q;
+    __device__ __forceinline__ uint4 get() const {
+        return make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                          pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
     }
+    __device__ __forceinline__ void load(const void* p) { set(load_stream(p)); }
+    __device__ __forceinline__ void store(void* p) const { store_stream(p, get()); }
     __device__ __forceinline__ static float round_io(float f) {
         return (float)(__bf16)f;
     }
@@ -127,8 +155,9 @@ __device__ __forceinline__ void load_params(const float* p, float (&out)[N]) {
 template <int N> struct MaskBytes;
 template <> struct MaskBytes<4> {
     __device__ __forceinline__ static void store(uint8_t* p, uint32_t bits) {
-        *reinterpret_cast<uint32_t*>(p) =
-            (bits & 1u) | ((bits >> 1) & 1u) << 8 | ((bits >> 2) & 1u) << 16 | ((bits >> 3) & 1u) << 24;
+        __builtin_nontemporal_store(
+            (bits & 1u) | ((bits >> 1) & 1u) << 8 | ((bits >> 2) & 1u) << 16 | ((bits >> 3) & 1u) << 24,
+            reinterpret_cast<uint32_t*>(p));
     }
     // any nonzero byte means keep
     __device__ __forceinline__ static uint32_t from_word(uint32_t w) {
@@ -145,11 +174,48 @@ template <> struct MaskBytes<8> {
                             ((bits >> 3) & 1u) << 24;
         const uint32_t hi = ((bits >> 4) & 1u) | ((bits >> 5) & 1u) << 8 | ((bits >> 6) & 1u) << 16 |
                             ((bits >> 7) & 1u) << 24;
-        *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
+        __builtin_nontemporal_store(lo, reinterpret_cast<uint32_t*>(p));
+        __builtin_nontemporal_store(hi, reinterpret_cast<uint32_t*>(p) + 1);
     }
     __device__ __forceinline__ static uint32_t load(const uint8_t* p) {
         const uint2 w = *reinterpret_cast<const uint2*>(p);
         return MaskBytes<4>::from_word(w.x) | (MaskBytes<4>::from_word(w.y) << 4);
+    }
+};
+
+// h of one vector: the stored words (for the h store) and the stored
+// values widened back to fp32 (what the norm reads).
+template <typename IO> struct HVec;
+template <> struct HVec<__bf16> {
+    __device__ __forceinline__ static void compute(uint4 xq, uint4 rq, const float (&b)[8],
+                                                   const bool (&keep)[8], float scale,
+                                                   uint4& hw, float (&hr)[8]) {
+        const uint32_t xw[4] = {xq.x, xq.y, xq.z, xq.w}, rw[4] = {rq.x, rq.y, rq.z, rq.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const float h0 = residual_dropout(bf16_lo(xw[p]), b[2 * p], bf16_lo(rw[p]),
+                                              keep[2 * p], scale);
+            const float h1 = residual_dropout(bf16_hi(xw[p]), b[2 * p + 1], bf16_hi(rw[p]),
+                                              keep[2 * p + 1], scale);
+            o[p] = pack_bf16x2(h0, h1);          // round to nearest even, two at a time
+            hr[2 * p] = bf16_lo(o[p]);
+            hr[2 * p + 1] = bf16_hi(o[p]);
+        }
+        hw = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+};
+template <> struct HVec<float> {
+    __device__ __forceinline__ static void compute(uint4 xq, uint4 rq, const float (&b)[4],
+                                                   const bool (&keep)[4], float scale,
+                                                   uint4& hw, float (&hr)[4]) {
+        const uint32_t xw[4] = {xq.x, xq.y, xq.z, xq.w}, rw[4] = {rq.x, rq.y, rq.z, rq.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            hr[j] = residual_dropout(__uint_as_float(xw[j]), b[j], __uint_as_float(rw[j]),
+                                     keep[j], scale);
+        hw = make_uint4(__float_as_uint(hr[0]), __float_as_uint(hr[1]), __float_as_uint(hr[2]),
+                        __float_as_uint(hr[3]));
     }
 };
 
@@ -174,6 +240,40 @@ __device__ __forceinline__ float block_sum(float v, float* slot, int nwaves) {
     float s = slot[0];
     for (int w = 1; w < nwaves; ++w) s += slot[w];
     return s;
+}
+
+// Running (count, mean, M2) of a set of values; merge() is Chan, Golub and
+// LeVeque's pairwise update.  merge(a, b) is evaluated with `a` the operand
+// from the lower lane (or earlier wave), so both butterfly partners compute
+// the same expression and end with the same bits.
+struct MeanM2 {
+    float n, mean, m2;
+};
+__device__ __forceinline__ MeanM2 merge(MeanM2 a, MeanM2 b) {
+    const float n = a.n + b.n;
+    const float wb = n > 0.0f ? __fdividef(b.n, n) : 0.0f;   // both empty: stays (0, 0, 0)
+    const float d = b.mean - a.mean;
+    return {n, a.mean + d * wb, a.m2 + b.m2 + d * d * a.n * wb};
+}
+
+// Team-wide merge of per-thread (count, mean, M2): wave butterflies, then the
+// waves' results in wave order through `slot` (3 x 16 floats of LDS).
+__device__ __forceinline__ MeanM2 block_mean_m2(MeanM2 v, float* slot, int nwaves) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int off = 1; off <= 32; off <<= 1) {
+        const MeanM2 o{__shfl_xor(v.n, off, 64), __shfl_xor(v.mean, off, 64),
+                       __shfl_xor(v.m2, off, 64)};
+        const bool upper = (lane & off) != 0;
+        v = merge(upper ? o : v, upper ? v : o);
+    }
+    if (nwaves == 1) return v;
+    const int wave = threadIdx.x >> 6;
+    if (lane == 0) { slot[wave] = v.n; slot[16 + wave] = v.mean; slot[32 + wave] = v.m2; }
+    __syncthreads();
+    MeanM2 acc{slot[0], slot[16], slot[32]};
+    for (int w = 1; w < nwaves; ++w) acc = merge(acc, MeanM2{slot[w], slot[16 + w], slot[32 + w]});
+    return acc;
 }
 
 // Two sums at once (16 + 16 floats of LDS).

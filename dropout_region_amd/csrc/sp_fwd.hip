@@ -19,12 +19,19 @@
 namespace spr {
 
 // WAVE_ROWS: each wave owns one row (short rows, 4 rows per workgroup, no
-// LDS); otherwise the whole workgroup owns one row.
-template <typename IO, int NORM, bool DROP, int VPT, bool WAVE_ROWS, int LB>
+// LDS); otherwise the whole workgroup owns one row.  EXACT: the row is
+// exactly VPT vectors per thread, so no slot is idle.
+//
+// Every load is issued unconditionally (a ragged row's idle slots re-read its
+// last vector and are masked afterwards), so a thread has all its x and
+// residual vectors in flight at once; the dropout words, which need no
+// data, are computed while they arrive.  Statistics: each thread reduces
+// its own values to (count, mean, M2), then one Chan merge over the team.
+template <typename IO, int NORM, bool DROP, int VPT, bool WAVE_ROWS, int LB, bool EXACT>
 __global__ void __launch_bounds__(LB) sp_region_fwd_kernel(FwdArgs a) {
-    using V = Vec<IO>;
-    constexpr int E = V::N;
-    __shared__ float red[2][16];
+    constexpr int E = Vec<IO>::N;
+    constexpr int MW = E / 4;                 // mask words per vector
+    __shared__ float red[48];
 
     int tid, tpr, nwaves;
     int64_t row;
@@ -43,31 +50,50 @@ __global__ void __launch_bounds__(LB) sp_region_fwd_kernel(FwdArgs a) {
     // by part of a team.
     if (row >= a.rows) return;
 
-    const IO* xr = static_cast<const IO*>(a.x) + row * a.hidden;
-    const IO* rr = static_cast<const IO*>(a.residual) + row * a.hidden;
+    const int64_t rbase = row * a.hidden;
+    const IO* xr = static_cast<const IO*>(a.x) + rbase;
+    const IO* rr = static_cast<const IO*>(a.residual) + rbase;
 
-    V xv[VPT], rv[VPT];
+    int vc[VPT];
+    bool ok[VPT];
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
         const int vec = k * tpr + tid;
-        if (vec < a.nvec) {
-            xv[k].load(xr + (int64_t)vec * E);
-            rv[k].load(rr + (int64_t)vec * E);
-        }
+        ok[k] = EXACT || vec < a.nvec;
+        vc[k] = ok[k] ? vec : a.nvec - 1;
+    }
+
+    uint4 xq[VPT], rq[VPT];
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+        xq[k] = load_stream(xr + (int64_t)vc[k] * E);
+        rq[k] = load_stream(rr + (int64_t)vc[k] * E);
+    }
+    float bb[VPT][E];
+    if (a.bias) {
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) load_params<E>(a.bias + (int64_t)vc[k] * E, bb[k]);
+    } else {
+#pragma unroll
+        for (int k = 0; k < VPT; ++k)
+#pragma unroll
+            for (int j = 0; j < E; ++j) bb[k][j] = 0.0f;
     }
 
     // Dropout decisions: element (row, c) is element e = (row_base+row)*h + c
     // of the full tensor; its word is word e%4 of Philox block e/4.
-    uint32_t kb[VPT];
-    if (DROP) {
-        const uint64_t e_row = (a.row_base + (uint64_t)row) * (uint64_t)a.hidden;
+    bool keep[VPT][E];
 #pragma unroll
-        for (int k = 0; k < VPT; ++k) {
-            const int vec = k * tpr + tid;
-            const uint64_t blk = (e_row + (uint64_t)vec * E) >> 2;
-            uint32_t bits = keep4(blk, a.off_lo, a.off_hi, a.key_lo, a.key_hi, a.thr);
-            if (E == 8) bits |= keep4(blk + 1, a.off_lo, a.off_hi, a.key_lo, a.key_hi, a.thr) << 4;
-            kb[k] = bits;
+    for (int k = 0; k < VPT; ++k) {
+        if (DROP) {
+            const uint64_t e0 = (a.row_base + (uint64_t)row) * (uint64_t)a.hidden +
+                                (uint64_t)vc[k] * E;
+#pragma unroll
+            for (int q = 0; q < MW; ++q)
+                keep4((e0 >> 2) + q, a.off_lo, a.off_hi, a.key_lo, a.key_hi, a.thr, &keep[k][4 * q]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < E; ++j) keep[k][j] = true;   // p == 0: scale is exactly 1
         }
     }
 
@@ -75,66 +101,73 @@ __global__ void __launch_bounds__(LB) sp_region_fwd_kernel(FwdArgs a) {
     float sum = 0.0f;
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
-        const int vec = k * tpr + tid;
-        if (vec < a.nvec) {
-            float bb[E];
-            if (a.bias) {
-                load_params<E>(a.bias + (int64_t)vec * E, bb);
-            } else {
+        uint4 hw;
+        HVec<IO>::compute(xq[k], rq[k], bb[k], keep[k], DROP ? a.scale : 1.0f, hw, hv[k]);
+        if (ok[k]) {
 #pragma unroll
-                for (int j = 0; j < E; ++j) bb[j] = 0.0f;
-            }
-            V hvec;
+            for (int j = 0; j < E; ++j) sum += hv[k][j];
+            const int64_t off = rbase + (int64_t)vc[k] * E;
+            store_stream(static_cast<IO*>(a.h_out) + off, hw);
+            if (DROP) {
 #pragma unroll
-            for (int j = 0; j < E; ++j) {
-                // p == 0: every element is kept and scale is exactly 1
-                const bool keep = DROP ? ((kb[k] >> j) & 1u) != 0 : true;
-                const float hr = V::round_io(
-                    residual_dropout(xv[k].v[j], bb[j], rv[k].v[j], keep, DROP ? a.scale : 1.0f));
-                hv[k][j] = hr;
-                hvec.v[j] = hr;
-                sum += hr;
-            }
-            const int64_t off = row * a.hidden + (int64_t)vec * E;
-            hvec.store(static_cast<IO*>(a.h_out) + off);
-            if (DROP) MaskBytes<E>::store(a.mask_out + off, kb[k]);
-        } else {
-#pragma unroll
-            for (int j = 0; j < E; ++j) hv[k][j] = 0.0f;
-        }
-    }
-
-    float mean = 0.0f;
-    if (NORM == SPR_LAYERNORM) mean = block_sum(sum, red[0], nwaves) * a.inv_h;
-    float sq = 0.0f;
-#pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-        const int vec = k * tpr + tid;
-        if (vec < a.nvec) {
-#pragma unroll
-            for (int j = 0; j < E; ++j) {
-                const float d = hv[k][j] - mean;
-                sq += d * d;
+                for (int q = 0; q < MW; ++q)
+                    __builtin_nontemporal_store(mask_word(&keep[k][4 * q]),
+                                                reinterpret_cast<uint32_t*>(a.mask_out + off) + q);
             }
         }
     }
-    sq = block_sum(sq, red[1], nwaves);
-    const float rstd = rsqrtf(sq * a.inv_h + a.eps);
+
+    float g[VPT][E], bt[VPT][E];
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+        load_params<E>(a.gamma + (int64_t)vc[k] * E, g[k]);
+        if (NORM == SPR_LAYERNORM) load_params<E>(a.beta + (int64_t)vc[k] * E, bt[k]);
+    }
+
+    float mean = 0.0f, var;
+    if (NORM == SPR_LAYERNORM) {
+        float n = 0.0f;
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) n += ok[k] ? (float)E : 0.0f;
+        const float m_loc = n > 0.0f ? sum / n : 0.0f;
+        float m2 = 0.0f;
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) {
+            if (ok[k]) {
+#pragma unroll
+                for (int j = 0; j < E; ++j) {
+                    const float d = hv[k][j] - m_loc;
+                    m2 = fmaf(d, d, m2);
+                }
+            }
+        }
+        const MeanM2 st = block_mean_m2(MeanM2{n, m_loc, m2}, red, nwaves);
+        mean = st.mean;
+        var = st.m2 * a.inv_h;
+    } else {
+        float sq = 0.0f;
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) {
+            if (ok[k]) {
+#pragma unroll
+                for (int j = 0; j < E; ++j) sq = fmaf(hv[k][j], hv[k][j], sq);
+            }
+        }
+        var = block_sum(sq, red, nwaves) * a.inv_h;     // mean square
+    }
+    const float rstd = rsqrtf(var + a.eps);
+    const float shift = -mean * rstd;                   // xhat = h * rstd + shift
 
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
-        const int vec = k * tpr + tid;
-        if (vec < a.nvec) {
-            float g[E], b[E];
-            load_params<E>(a.gamma + (int64_t)vec * E, g);
-            if (NORM == SPR_LAYERNORM) load_params<E>(a.beta + (int64_t)vec * E, b);
-            V yv;
+        if (ok[k]) {
+            Vec<IO> yv;
 #pragma unroll
             for (int j = 0; j < E; ++j) {
-                const float xh = (hv[k][j] - mean) * rstd;
-                yv.v[j] = (NORM == SPR_LAYERNORM) ? xh * g[j] + b[j] : xh * g[j];
+                const float xh = fmaf(hv[k][j], rstd, shift);
+                yv.v[j] = (NORM == SPR_LAYERNORM) ? fmaf(xh, g[k][j], bt[k][j]) : xh * g[k][j];
             }
-            yv.store(static_cast<IO*>(a.y_out) + row * a.hidden + (int64_t)vec * E);
+            yv.store(static_cast<IO*>(a.y_out) + rbase + (int64_t)vc[k] * E);
         }
     }
     if (tid == 0) {
@@ -143,15 +176,15 @@ __global__ void __launch_bounds__(LB) sp_region_fwd_kernel(FwdArgs a) {
     }
 }
 
-template <typename IO, int NORM, bool DROP, bool WR>
+template <typename IO, int NORM, bool DROP, bool WR, bool EXACT>
 static hipError_t fwd_by_vpt(const RowPlan& p, const FwdArgs& a, hipStream_t s) {
     const int64_t grid = WR ? (a.rows + p.rpw - 1) / p.rpw : a.rows;
     const dim3 g((unsigned)grid), b((unsigned)p.block);
 #define SPR_FWD_CASE(V, L)                                                                    \
     case V:                                                                                   \
-        hipLaunchKernelGGL((sp_region_fwd_kernel<IO, NORM, DROP, V, WR, L>), g, b, 0, s, a);  \
+        hipLaunchKernelGGL((sp_region_fwd_kernel<IO, NORM, DROP, V, WR, L, EXACT>), g, b, 0, s, a); \
         break;
-    if (WR) {
+    if constexpr (WR) {
         switch (p.vpt) {
             SPR_FWD_CASE(1, 256) SPR_FWD_CASE(2, 256) SPR_FWD_CASE(3, 256) SPR_FWD_CASE(4, 256)
             default: return hipErrorInvalidValue;
@@ -170,8 +203,12 @@ static hipError_t fwd_by_vpt(const RowPlan& p, const FwdArgs& a, hipStream_t s) 
 
 template <typename IO, int NORM, bool DROP>
 static hipError_t fwd_by_mode(const RowPlan& p, const FwdArgs& a, hipStream_t s) {
-    return p.rpw > 1 ? fwd_by_vpt<IO, NORM, DROP, true>(p, a, s)
-                     : fwd_by_vpt<IO, NORM, DROP, false>(p, a, s);
+    const bool exact = p.nvec == p.vpt * p.tpr;
+    if (p.rpw > 1)
+        return exact ? fwd_by_vpt<IO, NORM, DROP, true, true>(p, a, s)
+                     : fwd_by_vpt<IO, NORM, DROP, true, false>(p, a, s);
+    return exact ? fwd_by_vpt<IO, NORM, DROP, false, true>(p, a, s)
+                 : fwd_by_vpt<IO, NORM, DROP, false, false>(p, a, s);
 }
 
 template <typename IO, int NORM>

@@ -31,6 +31,10 @@ struct VptBound {
 };
 static constexpr VptBound kWgCombos[] = {{1, 1024}, {2, 1024}, {3, 1024}, {4, 1024},
                                          {5, 768},  {6, 768},  {8, 512}};
+// The backward runs one workgroup per CU, keeps three column accumulators
+// per element in registers, so its bound tracks the workgroup it needs.
+static constexpr VptBound kBwdCombos[] = {{1, 1024}, {2, 768}, {3, 512}, {4, 512},
+                                          {5, 640},  {6, 512}, {8, 512}};
 
 enum PlanKind { kPlanForward, kPlanBackward };
 

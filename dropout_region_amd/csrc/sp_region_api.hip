@@ -35,7 +35,7 @@ bool make_row_plan(int io, int64_t h, PlanKind kind, RowPlan* plan) {
     for (int i = 0; i < 7; ++i) {
         const int v = order[i];
         int lb = 0;
-        for (const VptBound& c : kWgCombos)
+        for (const VptBound& c : (kind == kPlanForward) ? kWgCombos : kBwdCombos)
             if (c.vpt == v) lb = c.lb;
         const int64_t tpr = ((nvec + v - 1) / v + 63) / 64 * 64;
         if (tpr > lb) continue;
