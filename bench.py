@@ -1,20 +1,26 @@
 """Benchmark of the SP-region forward + backward on one MI355X.
 
 A step is one pass of the whole region -- sp_region_fwd then sp_region_bwd --
-over one token shard that is already resident in HBM.  The default workload
-is one rank's shard of a 22B-class layer boundary (h=6144, s=2048, b=4,
-t=8: [256, 4, 6144], bf16 I/O, LayerNorm, p=0.1).  Inputs are seeded
-synthetic draws (sp_inputs.py).  Buffer sets are rotated so that the working
-set of consecutive steps exceeds the 256 MB Infinity Cache.
+over one token shard already resident in HBM.  The default workload is one
+rank's shard of a 22B-class layer boundary (h=6144, s=2048, b=4, t=8:
+[256, 4, 6144], bf16 I/O, LayerNorm, p=0.1).  Inputs are seeded synthetic
+draws (sp_inputs.py).  Buffer sets are rotated so that consecutive steps miss
+the 256 MB Infinity Cache.
 
 Prints one JSON line: tokens/s, HBM GB/s and fraction of the 8 TB/s peak
-from algorithmic bytes, per-call times measured with HIP events on the
-launch stream, the roofline record of the dominant kernel, and the CPU
-oracle timed on the host (a baseline, not a target).
+from algorithmic bytes, the per-kernel times measured with HIP events on the
+launch stream, the roofline record of the dominant kernel (with the HBM
+traffic of the committed rocprofv3 counter summary, if it was taken on the
+current kernel sources), and the CPU oracle timed on the host.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py --pmc-summary FETCH_DIR WRITE_DIR    (writes profiles/..._hbm_traffic.json)
+    python bench.py --stats-summary TRACE_DIR            (writes profiles/..._kernel_stats.md)
 """
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -26,6 +32,17 @@ if ROOT not in sys.path:
 
 PEAK_HBM_GBPS = 8000.0           # MI355X HBM3E
 METRIC = "tokens/s and achieved HBM GB/s (% of peak) for SP-region fwd+bwd, 1 GPU"
+PROFILES = os.path.join(ROOT, "profiles")
+COPY_BYTES = 1 << 30             # the plain copy the counters are calibrated on
+
+
+def kernel_source_hash():
+    """Hash of the HIP sources: counter figures taken on other sources are stale."""
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "dropout_region_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def algorithmic_bytes(w, with_bias=True, with_dh_out=False):
@@ -35,7 +52,9 @@ def algorithmic_bytes(w, with_bias=True, with_dh_out=False):
               (1 B/elem when p > 0), read bias/gamma/beta, write mean/rstd
     backward: read dy, h (2 es/elem), mask (1 B/elem), [dh_out] (es/elem),
               write dx, dres (2 es/elem), read gamma and the stats, write
-              dgamma, dbeta, dbias"""
+              dgamma, dbeta, dbias
+    Returns (fwd, bwd_rows, bwd_grads): bwd_rows is what the backward's row
+    pass moves, bwd_grads the three gradient rows the finalize writes."""
     E, N, H = w.elems, w.rows, w.h
     es = 2 if w.io == 1 else 4
     m = 1 if w.p > 0 else 0
@@ -44,14 +63,14 @@ def algorithmic_bytes(w, with_bias=True, with_dh_out=False):
     n_stat = 2 if ln else 1
     fwd = E * (4 * es + m) + n_par * H * 4 + n_stat * N * 4
     n_grad = 1 + (1 if ln else 0) + 1
-    bwd = E * (4 * es + m + (es if with_dh_out else 0)) + n_stat * N * 4 + H * 4 + n_grad * H * 4
-    return fwd, bwd
+    bwd_rows = E * (4 * es + m + (es if with_dh_out else 0)) + n_stat * N * 4 + H * 4
+    return fwd, bwd_rows, n_grad * H * 4
 
 
 def cpu_baseline(w, min_seconds=10.0, max_seconds=30.0):
     """The CPU oracle (single-threaded C, as it stands) on the same shard:
     forward + backward over all N rows, repeated until at least min_seconds
-    of CPU time have passed.  Returns tokens/s and the sample description."""
+    have passed.  Returns tokens/s and the sample description."""
     import oracle
     from oracle import build as obuild
     from sp_inputs import make_inputs
@@ -73,8 +92,9 @@ def cpu_baseline(w, min_seconds=10.0, max_seconds=30.0):
                       f"({t_total:.1f} s, 1 thread)"}
 
 
-def copy_bandwidth(torch, nbytes=1 << 30, iters=20):
-    """GB/s (read + write) of torch's device copy of a 1 GiB buffer."""
+def copy_bandwidth(torch, nbytes=COPY_BYTES, iters=20):
+    """GB/s (read + write) of torch's device copy of a 1 GiB buffer (the HIP
+    runtime's blit kernel): the plain copy the HBM counters are scaled by."""
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
     for _ in range(3):
@@ -91,6 +111,77 @@ def copy_bandwidth(torch, nbytes=1 << 30, iters=20):
     return 2 * nbytes / sec / 1e9
 
 
+# ------------------------------------------------------------------ summaries
+def _profile_name(workload, what):
+    return os.path.join(PROFILES, f"sp_region_{workload}_{what}")
+
+
+def _short(name):
+    """Readable kernel name: sp_region_fwd_kernel etc. (template arguments dropped)."""
+    for base in ("sp_region_fwd_kernel", "sp_region_bwd_rows_kernel", "sp_region_bwd_rowsum_kernel",
+                 "sp_region_bwd_main_kernel", "sp_region_bwd_finalize_kernel"):
+        if base in name:
+            return base
+    return name
+
+
+def pmc_summary(fetch_dir, write_dir, workload, command):
+    """Per-kernel HBM bytes per dispatch from two rocprofv3 --pmc runs
+    (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), scaled by what the same
+    counter reads for the 1 GiB plain copy of the same run."""
+    def load(d, counter):
+        rows = list(csv.DictReader(open(glob.glob(os.path.join(d, "*counter_collection.csv"))[0])))
+        by = {}
+        for r in rows:
+            if r["Counter_Name"] == counter:
+                by.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]) * 1024.0)
+        return by
+    fetch, write = load(fetch_dir, "FETCH_SIZE"), load(write_dir, "WRITE_SIZE")
+    copy_name = [k for k in fetch if "copyBuffer" in k][0]
+    f_scale = COPY_BYTES / max(fetch[copy_name])
+    w_scale = COPY_BYTES / max(write[copy_name])
+    out = {"command": command, "source_hash": kernel_source_hash(), "workload": workload,
+           "copy_kernel": copy_name, "copy_bytes": COPY_BYTES,
+           "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4), "kernels": {}}
+    for k in fetch:
+        if "sp_region" not in k:
+            continue
+        wv = write.get(k, [0.0])
+        out["kernels"][_short(k)] = {
+            "fetch_bytes": round(sum(fetch[k]) / len(fetch[k]) * f_scale),
+            "write_bytes": round(sum(wv) / len(wv) * w_scale), "dispatches": len(fetch[k])}
+    path = _profile_name(workload, "hbm_traffic.json")
+    json.dump(out, open(path, "w"), indent=1)
+    print(path)
+
+
+def stats_summary(trace_dir, workload, command):
+    """Markdown table of a rocprofv3 --kernel-trace --stats run."""
+    rows = list(csv.DictReader(open(glob.glob(os.path.join(trace_dir, "*kernel_stats.csv"))[0])))
+    lines = [f"# rocprofv3 kernel statistics: {workload}", "",
+             "Command (from the repository root, on the GPU box):", "", "```", command, "```", "",
+             f"Kernel sources: `{kernel_source_hash()}` (hash of dropout_region_amd/csrc/*)", "",
+             "| Kernel | Calls | Average ns | Min ns | Max ns | Share % |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| {_short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']):.0f} | "
+                     f"{float(r['MinNs']):.0f} | {float(r['MaxNs']):.0f} | "
+                     f"{float(r['Percentage']):.2f} |")
+    path = _profile_name(workload, "kernel_stats.md")
+    open(path, "w").write("\n".join(lines) + "\n")
+    print(path)
+
+
+def load_traffic(workload):
+    """Measured HBM bytes per dispatch by kernel, or None when no summary was
+    taken on the current kernel sources."""
+    path = _profile_name(workload, "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    t = json.load(open(path))
+    return t["kernels"] if t.get("source_hash") == kernel_source_hash() else None
+
+
+# ------------------------------------------------------------------ bench
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -100,7 +191,17 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--min-set-bytes", type=float, default=1.0, help="GiB of rotated buffers")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--stats-summary", metavar="TRACE_DIR")
+    ap.add_argument("--command", default="", help="command recorded in a summary")
     args = ap.parse_args()
+
+    from sp_inputs import HEADLINE, WORKLOADS
+    wname = args.workload or HEADLINE
+    if args.pmc_summary:
+        return pmc_summary(*args.pmc_summary, wname, args.command)
+    if args.stats_summary:
+        return stats_summary(args.stats_summary, wname, args.command)
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
               "(the region is per-rank; there are no collectives to run)", file=sys.stderr)
@@ -109,10 +210,10 @@ def main():
     import numpy as np
     import torch
     import dropout_region_amd as spr
-    from sp_inputs import HEADLINE, WORKLOADS, make_inputs
+    from sp_inputs import make_inputs
     from tests import parity as P
 
-    w = WORKLOADS[args.workload or HEADLINE]
+    w = WORKLOADS[wname]
     dev = torch.device("cuda:0")
     d = spr.Desc(s_local=w.s_local, b=w.b, h=w.h, shard_index=0, t=w.t, io=w.io, norm=w.norm,
                  p=w.p, eps=w.eps, seed=w.seed, offset=0)
@@ -152,15 +253,18 @@ def main():
         s.update({("b_" + k): v for k, v in spr.alloc_bwd_outputs(d, dev).items()})
         sets.append(s)
     stream = torch.cuda.current_stream()
+    n_bwd = spr.sp_region_bwd_num_launches(d)
 
     def fwd(s):
         spr.sp_region_fwd(d, s["x"], bias, s["res"], gamma, beta, s["h"], s["y"], s["mask"],
                           s["mean"], s["rstd"], stream)
 
+    def bwd_args(s):
+        return (s["dy"], None, s["h"], s["mask"], s["mean"], s["rstd"], gamma, s["b_dx"],
+                s["b_dres"], s["b_dgamma"], s["b_dbeta"], s["b_dbias"], s["b_workspace"])
+
     def bwd(s):
-        spr.sp_region_bwd(d, s["dy"], None, s["h"], s["mask"], s["mean"], s["rstd"], gamma,
-                          s["b_dx"], s["b_dres"], s["b_dgamma"], s["b_dbeta"], s["b_dbias"],
-                          s["b_workspace"], stream)
+        spr.sp_region_bwd(d, *bwd_args(s), stream)
 
     for i in range(args.warmup):
         fwd(sets[i % nsets])
@@ -180,46 +284,61 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = ev0.elapsed_time(ev1) / args.steps
 
-    # ---- timed region 2: HIP events around each call on the launch stream
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # ---- timed region 2: HIP events around each kernel launch on the stream
+    # (the backward run one launch at a time -- the same launches in order)
+    nk = 1 + n_bwd
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(args.steps)]
     for i in range(args.steps):
         s = sets[i % nsets]
         evs[i][0].record(stream)
         fwd(s)
         evs[i][1].record(stream)
-        bwd(s)
-        evs[i][2].record(stream)
+        for k in range(n_bwd):
+            spr.sp_region_bwd_launch(d, k, *bwd_args(s), stream)
+            evs[i][2 + k].record(stream)
     torch.cuda.synchronize()
-    fwd_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    bwd_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    per_kernel_ms = np.array([[e[k].elapsed_time(e[k + 1]) for k in range(nk)] for e in evs])
+    kernel_us = per_kernel_ms.mean(axis=0) * 1e3
+    names = ["sp_region_fwd_kernel"] + (
+        ["sp_region_bwd_rows_kernel", "sp_region_bwd_finalize_kernel"] if n_bwd == 2 else
+        ["sp_region_bwd_rowsum_kernel", "sp_region_bwd_main_kernel", "sp_region_bwd_finalize_kernel"])
+    fwd_b, bwd_rows_b, bwd_grad_b = algorithmic_bytes(w)
+    # algorithmic bytes of each launch (the split path's row-sum pass only re-reads)
+    alg = [fwd_b] + ([bwd_rows_b, bwd_grad_b] if n_bwd == 2 else [0, bwd_rows_b, bwd_grad_b])
 
-    fwd_b, bwd_b = algorithmic_bytes(w)
     tokens_per_s = w.rows / (ms_per_step / 1e3)
-    gbps = (fwd_b + bwd_b) / (ms_per_step / 1e3) / 1e9
-    f_us, b_us = float(np.mean(fwd_ms) * 1e3), float(np.mean(bwd_ms) * 1e3)
-    dom, dom_b, dom_us = ("sp_region_bwd", bwd_b, b_us) if b_us >= f_us else ("sp_region_fwd", fwd_b, f_us)
-    achieved = dom_b / (dom_us / 1e6) / 1e9
+    total_alg = fwd_b + bwd_rows_b + bwd_grad_b
+    gbps = total_alg / (ms_per_step / 1e3) / 1e9
+    dom = int(np.argmax(kernel_us))
+    achieved = alg[dom] / (kernel_us[dom] / 1e6) / 1e9
+    traffic = load_traffic(w.name)
+    dom_traffic = None
+    if traffic and names[dom] in traffic:
+        t = traffic[names[dom]]
+        dom_traffic = t["fetch_bytes"] + t["write_bytes"]
     copy_gbps = copy_bandwidth(torch)
 
     out = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if w.io == 1 else "f32",
-        "data": "synthetic",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.io == 1 else "f32", "data": "synthetic",
         "config": {"workload": w.name, "shard": [w.s_local, w.b, w.h], "t": w.t,
                    "norm": "layernorm" if w.norm == 0 else "rmsnorm", "p": w.p, "eps": w.eps,
                    "io": "bf16" if w.io == 1 else "fp32", "params_and_stats": "fp32",
                    "tokens_per_step": w.rows, "buffer_sets": nsets},
         "hbm_gbps": round(gbps, 1), "hbm_frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4),
         "copy_gbps": round(copy_gbps, 1), "frac_of_copy": round(gbps / copy_gbps, 4),
-        "fwd_us": round(f_us, 2), "bwd_us": round(b_us, 2),
-        "fwd_us_p10_p90": [round(float(np.percentile(fwd_ms, q)) * 1e3, 2) for q in (10, 90)],
-        "bwd_us_p10_p90": [round(float(np.percentile(bwd_ms, q)) * 1e3, 2) for q in (10, 90)],
-        "algorithmic_bytes": {"fwd": fwd_b, "bwd": bwd_b},
+        "bwd_path": os.environ.get("SPR_BWD_PATH", "auto"),
+        "kernels_us": {n: round(float(u), 2) for n, u in zip(names, kernel_us)},
+        "kernels_us_p10_p90": {n: [round(float(np.percentile(per_kernel_ms[:, k], q)) * 1e3, 2)
+                                   for q in (10, 90)] for k, n in enumerate(names)},
+        "algorithmic_bytes": {"fwd": fwd_b, "bwd": bwd_rows_b + bwd_grad_b},
         "wall_s_timed_region": round(wall, 4),
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+        "roofline": {"bound": "hbm", "kernel": names[dom], "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
-                     "traffic": None},
+                     "traffic": dom_traffic, "algorithmic_bytes_per_launch": alg[dom],
+                     "launch_us": round(float(kernel_us[dom]), 2)},
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)

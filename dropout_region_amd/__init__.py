@@ -72,6 +72,10 @@ def lib():
         L.sp_region_fwd.restype = ctypes.c_int
         L.sp_region_bwd.argtypes = [D] + [P] * 12 + [P, ctypes.c_size_t, P]
         L.sp_region_bwd.restype = ctypes.c_int
+        L.sp_region_bwd_num_launches.argtypes = [D]
+        L.sp_region_bwd_num_launches.restype = ctypes.c_int
+        L.sp_region_bwd_launch.argtypes = [D, ctypes.c_int] + [P] * 12 + [P, ctypes.c_size_t, P]
+        L.sp_region_bwd_launch.restype = ctypes.c_int
         L.sp_region_bwd_workspace_bytes.argtypes = [D]
         L.sp_region_bwd_workspace_bytes.restype = ctypes.c_size_t
         L.sp_region_activation_bytes.argtypes = [D, P, P]
@@ -147,27 +151,45 @@ def sp_region_fwd(d, x, bias, residual, gamma, beta, h_out, y_out, mask_out, mea
         raise SprError("sp_region_fwd", st)
 
 
-def sp_region_bwd(d, dy, dh_out, h, mask, mean, rstd, gamma, dx_out, dres_out, dgamma_out,
-                  dbeta_out, dbias_out, workspace, stream=None):
+def _bwd_args(d, dy, dh_out, h, mask, mean, rstd, gamma, dx_out, dres_out, dgamma_out,
+              dbeta_out, dbias_out, workspace):
     import torch
-    L = lib()
     N, H, io, dev = d.rows, d.h, _io_dtype(d), dy.device if dy is not None else None
     f32, u8 = torch.float32, torch.uint8
     if workspace is None or not workspace.is_cuda or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous device tensor")
     ws_bytes = workspace.numel() * workspace.element_size()
-    args = [_arg(dy, "dy", N * H, io, dev), _arg(dh_out, "dh_out", N * H, io, dev, True),
+    return [_arg(dy, "dy", N * H, io, dev), _arg(dh_out, "dh_out", N * H, io, dev, True),
             _arg(h, "h", N * H, io, dev), _arg(mask, "mask", N * H, u8, dev, True),
             _arg(mean, "mean", N, f32, dev, True), _arg(rstd, "rstd", N, f32, dev),
             _arg(gamma, "gamma", H, f32, dev), _arg(dx_out, "dx_out", N * H, io, dev),
             _arg(dres_out, "dres_out", N * H, io, dev),
             _arg(dgamma_out, "dgamma_out", H, f32, dev),
             _arg(dbeta_out, "dbeta_out", H, f32, dev, True),
-            _arg(dbias_out, "dbias_out", H, f32, dev, True)]
-    st = L.sp_region_bwd(ctypes.byref(d.c()), *args, ctypes.c_void_p(workspace.data_ptr()),
-                         ctypes.c_size_t(ws_bytes), _stream(stream))
+            _arg(dbias_out, "dbias_out", H, f32, dev, True),
+            ctypes.c_void_p(workspace.data_ptr()), ctypes.c_size_t(ws_bytes)]
+
+
+def sp_region_bwd(d, dy, dh_out, h, mask, mean, rstd, gamma, dx_out, dres_out, dgamma_out,
+                  dbeta_out, dbias_out, workspace, stream=None):
+    args = _bwd_args(d, dy, dh_out, h, mask, mean, rstd, gamma, dx_out, dres_out, dgamma_out,
+                     dbeta_out, dbias_out, workspace)
+    st = lib().sp_region_bwd(ctypes.byref(d.c()), *args, _stream(stream))
     if st != SPR_OK:
         raise SprError("sp_region_bwd", st)
+
+
+def sp_region_bwd_num_launches(d):
+    return int(lib().sp_region_bwd_num_launches(ctypes.byref(d.c())))
+
+
+def sp_region_bwd_launch(d, index, dy, dh_out, h, mask, mean, rstd, gamma, dx_out, dres_out,
+                         dgamma_out, dbeta_out, dbias_out, workspace, stream=None):
+    args = _bwd_args(d, dy, dh_out, h, mask, mean, rstd, gamma, dx_out, dres_out, dgamma_out,
+                     dbeta_out, dbias_out, workspace)
+    st = lib().sp_region_bwd_launch(ctypes.byref(d.c()), int(index), *args, _stream(stream))
+    if st != SPR_OK:
+        raise SprError("sp_region_bwd_launch", st)
 
 
 # ------------------------------------------------------------ allocation helpers

@@ -195,11 +195,30 @@ __global__ void __launch_bounds__(256) sp_region_bwd_finalize_kernel(BwdArgs a) 
     const int64_t n3 = 3 * a.hidden;
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
     if (j < n3) {
+        // Group q's teams q, q+16, ... in order, four loads in flight at a
+        // time: stream i of the four takes every fourth of them, and the four
+        // streams are added pairwise at the end -- a fixed order.
         const float* p = a.partials + j;
-        for (int t = q; t < a.teams; t += kFinGroups) {
-            const float4 v = *reinterpret_cast<const float4*>(p + (int64_t)t * n3);
-            s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+        float4 s4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s4[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int t = q; t < a.teams; t += 4 * kFinGroups) {
+            float4 v[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int ti = t + i * kFinGroups;
+                v[i] = ti < a.teams ? *reinterpret_cast<const float4*>(p + (int64_t)ti * n3)
+                                    : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                s4[i].x += v[i].x; s4[i].y += v[i].y; s4[i].z += v[i].z; s4[i].w += v[i].w;
+            }
         }
+        s.x = (s4[0].x + s4[1].x) + (s4[2].x + s4[3].x);
+        s.y = (s4[0].y + s4[1].y) + (s4[2].y + s4[3].y);
+        s.z = (s4[0].z + s4[1].z) + (s4[2].z + s4[3].z);
+        s.w = (s4[0].w + s4[1].w) + (s4[2].w + s4[3].w);
     }
     part[q][lane] = s;
     __syncthreads();
@@ -214,6 +233,199 @@ __global__ void __launch_bounds__(256) sp_region_bwd_finalize_kernel(BwdArgs a) 
         float* out = k == 0 ? a.dgamma_out : (k == 1 ? a.dbeta_out : a.dbias_out);
         if (out) *reinterpret_cast<float4*>(out + c) = t;
     }
+}
+
+// ---------------------------------------------------------------- split path
+// Pass 1 (rowsum): one team per row, like the forward; reads dy and h and
+// writes the row's two sums sum_c g and sum_c g*xhat (g = dy*gamma) to
+// rowsum[row].  Pass 2 (main): tiles of tile_rows rows x one wave's 64
+// vectors (512 bf16 / 256 fp32 columns); the workgroup's 4 waves take rows
+// w, w + 4, ... and prefetch the next group of U rows while computing the
+// current one; dx/dresidual are written and the dgamma/dbeta/dbias column
+// partials of the tile's rows are added across the waves in wave order.
+constexpr int kSplitWaves = 4, kSplitUnroll = 4;
+
+template <typename IO, int NORM, int VPT, bool WAVE_ROWS, int LB, bool EXACT>
+__global__ void __launch_bounds__(LB) sp_region_bwd_rowsum_kernel(BwdArgs a) {
+    constexpr int E = Vec<IO>::N;
+    __shared__ float red[32];
+    int tid, tpr, nwaves;
+    int64_t row;
+    if (WAVE_ROWS) {
+        tid = threadIdx.x & 63;
+        tpr = 64;
+        nwaves = 1;
+        row = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    } else {
+        tid = threadIdx.x;
+        tpr = blockDim.x;
+        nwaves = blockDim.x >> 6;
+        row = blockIdx.x;
+    }
+    if (row >= a.rows) return;               // uniform per wave / workgroup
+
+    int vc[VPT];
+    bool ok[VPT];
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+        const int vec = k * tpr + tid;
+        ok[k] = EXACT || vec < a.nvec;
+        vc[k] = ok[k] ? vec : a.nvec - 1;
+    }
+    const int64_t rbase = row * a.hidden;
+    uint4 hq[VPT], dq[VPT];
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+        hq[k] = load_stream(static_cast<const IO*>(a.h) + rbase + (int64_t)vc[k] * E);
+        dq[k] = load_stream(static_cast<const IO*>(a.dy) + rbase + (int64_t)vc[k] * E);
+    }
+    float gam[VPT][E];
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) load_params<E>(a.gamma + (int64_t)vc[k] * E, gam[k]);
+    const float mu = (NORM == SPR_LAYERNORM) ? a.mean[row] : 0.0f;
+    const float rs = a.rstd[row];
+    float s1 = 0.0f, s2 = 0.0f;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+        Vec<IO> hv, dv;
+        hv.set(hq[k]);
+        dv.set(dq[k]);
+        if (ok[k]) {
+#pragma unroll
+            for (int j = 0; j < E; ++j) {
+                const float g = dv.v[j] * gam[k][j];
+                s1 += g;
+                s2 = fmaf(g, (hv.v[j] - mu) * rs, s2);
+            }
+        }
+    }
+    block_sum2(s1, s2, red, nwaves);
+    if (tid == 0) *reinterpret_cast<float2*>(a.rowpart + row * 2) = make_float2(s1, s2);
+}
+
+// Adds the 4 waves' column partials in wave order and writes them as
+// partial row `slot` of row block blockIdx.y: colpart[(rb*3 + slot)*h + c].
+template <int E>
+__device__ __forceinline__ void split_store_colpart(const BwdArgs& a, float (*sh)[64][E],
+                                                    const float (&acc)[E], int slot, int vec,
+                                                    bool ok) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int j = 0; j < E; ++j) sh[wave][lane][j] = acc[j];
+    __syncthreads();
+    if (wave == 0 && ok) {
+        float t[E];
+#pragma unroll
+        for (int j = 0; j < E; ++j) t[j] = sh[0][lane][j];
+        for (int w = 1; w < kSplitWaves; ++w)
+#pragma unroll
+            for (int j = 0; j < E; ++j) t[j] += sh[w][lane][j];
+        float* out = a.partials + ((int64_t)blockIdx.y * 3 + slot) * a.hidden + (int64_t)vec * E;
+#pragma unroll
+        for (int j = 0; j < E; j += 4)
+            *reinterpret_cast<float4*>(out + j) = make_float4(t[j], t[j + 1], t[j + 2], t[j + 3]);
+    }
+    __syncthreads();
+}
+
+// The saved tensors of one group of U rows of a pass-2 tile (one vector each).
+template <int U, int MW>
+struct TileIn {
+    uint4 h[U], dy[U], dho[U];
+    uint32_t mask[U][MW];
+    float mu[U], rs[U];
+    float2 rsum[U];
+};
+
+template <typename IO, int NORM, bool DROP>
+__global__ void __launch_bounds__(256) sp_region_bwd_main_kernel(BwdArgs a) {
+    using V = Vec<IO>;
+    constexpr int E = V::N, U = kSplitUnroll, MW = E / 4;
+    __shared__ float sh[kSplitWaves][64][E];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int vec = blockIdx.x * 64 + lane;
+    const bool ok = vec < a.nvec;
+    const int vcl = ok ? vec : a.nvec - 1;
+    float gam[E], acc_g[E], acc_b[E], acc_x[E];
+    load_params<E>(a.gamma + (int64_t)vcl * E, gam);
+#pragma unroll
+    for (int j = 0; j < E; ++j) acc_g[j] = acc_b[j] = acc_x[j] = 0.0f;
+
+    const int64_t r0 = (int64_t)blockIdx.y * a.tile_rows;
+    const int64_t r1 = r0 + a.tile_rows < a.rows ? r0 + a.tile_rows : a.rows;
+    constexpr int64_t step = kSplitWaves * U;
+
+    auto load_group = [&](int64_t base, TileIn<U, MW>& in) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t row = base + kSplitWaves * u;
+            const int64_t rc = row < r1 ? row : r1 - 1;          // clamp: always a valid row
+            const int64_t off = rc * a.hidden + (int64_t)vcl * E;
+            in.h[u] = load_stream(static_cast<const IO*>(a.h) + off);
+            in.dy[u] = load_stream(static_cast<const IO*>(a.dy) + off);
+            if (DROP) {
+#pragma unroll
+                for (int w = 0; w < MW; ++w)
+                    in.mask[u][w] = __builtin_nontemporal_load(
+                        reinterpret_cast<const uint32_t*>(a.mask + off) + w);
+            }
+            if (a.dh_out) in.dho[u] = load_stream(static_cast<const IO*>(a.dh_out) + off);
+            in.mu[u] = (NORM == SPR_LAYERNORM) ? a.mean[rc] : 0.0f;
+            in.rs[u] = a.rstd[rc];
+            in.rsum[u] = *reinterpret_cast<const float2*>(a.rowpart + rc * 2);
+        }
+    };
+
+    // Trip counts differ between waves (ragged tiles) but nothing in the loop
+    // synchronises the workgroup.
+    TileIn<U, MW> cur, nxt;
+    int64_t base = r0 + wave;
+    if (base < r1) load_group(base, cur);
+    for (; base < r1; base += step) {
+        if (base + step < r1) load_group(base + step, nxt);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t row = base + kSplitWaves * u;
+            const bool rok = row < r1;                       // wave-uniform
+            const float mg = cur.rsum[u].x * a.inv_h, mgx = cur.rsum[u].y * a.inv_h;
+            const float mu = cur.mu[u], rs = cur.rs[u];
+            V hv, dv, dho, dres, dx;
+            hv.set(cur.h[u]);
+            dv.set(cur.dy[u]);
+            if (a.dh_out) dho.set(cur.dho[u]);
+            uint32_t kb = 0xffu;
+            if (DROP) {
+                kb = MaskBytes<4>::from_word(cur.mask[u][0]);
+                if (MW == 2) kb |= MaskBytes<4>::from_word(cur.mask[u][MW - 1]) << 4;
+            }
+#pragma unroll
+            for (int j = 0; j < E; ++j) {
+                const float xh = (hv.v[j] - mu) * rs;
+                const float g = dv.v[j] * gam[j];
+                float dh = (NORM == SPR_LAYERNORM) ? rs * (g - mg - xh * mgx)
+                                                   : rs * (g - xh * mgx);
+                if (a.dh_out) dh += dho.v[j];
+                const float dxu = DROP ? (((kb >> j) & 1u) ? dh * a.scale : 0.0f) : dh;
+                dres.v[j] = dh;
+                dx.v[j] = dxu;
+                if (ok && rok) {
+                    acc_g[j] = fmaf(dv.v[j], xh, acc_g[j]);
+                    acc_b[j] += dv.v[j];
+                    acc_x[j] += dxu;
+                }
+            }
+            if (ok && rok) {
+                const int64_t off = row * a.hidden + (int64_t)vec * E;
+                dres.store(static_cast<IO*>(a.dres_out) + off);
+                dx.store(static_cast<IO*>(a.dx_out) + off);
+            }
+        }
+        cur = nxt;
+    }
+    split_store_colpart<E>(a, sh, acc_g, 0, vec, ok);
+    split_store_colpart<E>(a, sh, acc_b, 1, vec, ok);
+    split_store_colpart<E>(a, sh, acc_x, 2, vec, ok);
 }
 
 // Teams: one workgroup per CU (fewer workgroups cannot draw the full HBM
@@ -247,8 +459,10 @@ static hipError_t bwd_by_vpt(const RowPlan& p, const BwdArgs& a, hipStream_t s) 
         }
     }
 #undef SPR_BWD_CASE
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    return hipGetLastError();
+}
+
+static hipError_t launch_finalize(const BwdArgs& a, hipStream_t s) {
     const int64_t n3 = 3 * a.hidden;
     hipLaunchKernelGGL(sp_region_bwd_finalize_kernel, dim3((unsigned)((n3 + kFinCols - 1) / kFinCols)),
                        dim3(256), 0, s, a);
@@ -261,19 +475,80 @@ static hipError_t bwd_by_mode(const RowPlan& p, const BwdArgs& a, hipStream_t s)
                      : bwd_by_vpt<IO, NORM, DROP, false>(p, a, s);
 }
 
+template <typename IO, int NORM, bool WR, bool EXACT>
+static hipError_t rowsum_by_vpt(const RowPlan& p, const BwdArgs& a, hipStream_t s) {
+    const int64_t grid = WR ? (a.rows + p.rpw - 1) / p.rpw : a.rows;
+    const dim3 g((unsigned)grid), b((unsigned)p.block);
+#define SPR_RS_CASE(V, L)                                                                         \
+    case V:                                                                                       \
+        hipLaunchKernelGGL((sp_region_bwd_rowsum_kernel<IO, NORM, V, WR, L, EXACT>), g, b, 0, s, a); \
+        break;
+    if constexpr (WR) {
+        switch (p.vpt) {
+            SPR_RS_CASE(1, 256) SPR_RS_CASE(2, 256) SPR_RS_CASE(3, 256) SPR_RS_CASE(4, 256)
+            default: return hipErrorInvalidValue;
+        }
+    } else {
+        // must match kWgCombos (the forward's row plans)
+        switch (p.vpt) {
+            SPR_RS_CASE(1, 1024) SPR_RS_CASE(2, 1024) SPR_RS_CASE(3, 1024)
+            SPR_RS_CASE(4, 1024) SPR_RS_CASE(5, 768) SPR_RS_CASE(6, 768) SPR_RS_CASE(8, 512)
+            default: return hipErrorInvalidValue;
+        }
+    }
+#undef SPR_RS_CASE
+    return hipGetLastError();
+}
+
 template <typename IO, int NORM>
-static hipError_t bwd_by_drop(const spr_desc& d, const RowPlan& p, const BwdArgs& a, hipStream_t s) {
-    return d.p > 0.0f ? bwd_by_mode<IO, NORM, true>(p, a, s) : bwd_by_mode<IO, NORM, false>(p, a, s);
+static hipError_t split_rowsum(const BwdPlan& p, const BwdArgs& a, hipStream_t s) {
+    const RowPlan& rp = p.sum_rows;
+    const bool exact = rp.nvec == rp.vpt * rp.tpr;
+    if (rp.rpw > 1)
+        return exact ? rowsum_by_vpt<IO, NORM, true, true>(rp, a, s)
+                     : rowsum_by_vpt<IO, NORM, true, false>(rp, a, s);
+    return exact ? rowsum_by_vpt<IO, NORM, false, true>(rp, a, s)
+                 : rowsum_by_vpt<IO, NORM, false, false>(rp, a, s);
 }
 
-template <typename IO>
-static hipError_t bwd_by_norm(const spr_desc& d, const RowPlan& p, const BwdArgs& a, hipStream_t s) {
-    return d.norm == SPR_LAYERNORM ? bwd_by_drop<IO, SPR_LAYERNORM>(d, p, a, s)
-                                   : bwd_by_drop<IO, SPR_RMSNORM>(d, p, a, s);
+template <typename IO, int NORM>
+static hipError_t split_main(const spr_desc& d, const BwdPlan& p, const BwdArgs& a, hipStream_t s) {
+    const dim3 g((unsigned)p.col_tiles, (unsigned)p.row_blocks), b(256);
+    if (d.p > 0.0f)
+        hipLaunchKernelGGL((sp_region_bwd_main_kernel<IO, NORM, true>), g, b, 0, s, a);
+    else
+        hipLaunchKernelGGL((sp_region_bwd_main_kernel<IO, NORM, false>), g, b, 0, s, a);
+    return hipGetLastError();
 }
 
-hipError_t launch_bwd(const spr_desc& d, const RowPlan& p, const BwdArgs& a, hipStream_t s) {
-    return d.io == SPR_BF16 ? bwd_by_norm<__bf16>(d, p, a, s) : bwd_by_norm<float>(d, p, a, s);
+template <typename IO, int NORM>
+static hipError_t bwd_one(const spr_desc& d, const BwdPlan& p, const BwdArgs& a, hipStream_t s,
+                          int index) {
+    if (p.path == kBwdSplit) {
+        if (index == 0) return split_rowsum<IO, NORM>(p, a, s);
+        if (index == 1) return split_main<IO, NORM>(d, p, a, s);
+        return launch_finalize(a, s);
+    }
+    if (index == 0) return d.p > 0.0f ? bwd_by_mode<IO, NORM, true>(p.rows, a, s)
+                                      : bwd_by_mode<IO, NORM, false>(p.rows, a, s);
+    return launch_finalize(a, s);
+}
+
+int bwd_num_launches(const BwdPlan& p) { return p.path == kBwdSplit ? 3 : 2; }
+
+hipError_t launch_bwd(const spr_desc& d, const BwdPlan& p, const BwdArgs& a, hipStream_t s,
+                      int first, int last) {
+    for (int i = first; i < last; ++i) {
+        hipError_t e;
+        if (d.io == SPR_BF16)
+            e = d.norm == SPR_LAYERNORM ? bwd_one<__bf16, SPR_LAYERNORM>(d, p, a, s, i)
+                                        : bwd_one<__bf16, SPR_RMSNORM>(d, p, a, s, i);
+        else
+            e = d.norm == SPR_LAYERNORM ? bwd_one<float, SPR_LAYERNORM>(d, p, a, s, i)
+                                        : bwd_one<float, SPR_RMSNORM>(d, p, a, s, i);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace spr

@@ -75,7 +75,8 @@ struct BwdArgs {
     const float* gamma;
     void* dx_out;
     void* dres_out;
-    float* partials;       // [teams][3][h] fp32 column partials
+    float* partials;       // [teams][3][h] fp32 column partials (split path: [row_blocks][3][h])
+    float* rowpart;        // split path: [N] float2 row sums (sum g, sum g*xhat)
     float* dgamma_out;
     float* dbeta_out;
     float* dbias_out;
@@ -85,12 +86,42 @@ struct BwdArgs {
     float inv_h;
     int nvec;
     int teams;             // row teams in the grid = partial rows
+    int col_tiles;         // split path: tiles of one wave's 64 vectors across a row
+    int tile_rows;         // split path: rows per tile
 };
+
+// The backward's two strategies.
+//  fused: one persistent workgroup per CU owns whole rows; its register column
+//         partials make one partial row of 3*h fp32 per workgroup.
+//  split: a read-only pass over dy and h gives each row its two sums; a
+//         second pass over column tiles writes dx, dresidual and the
+//         dgamma/dbeta/dbias partials of its rows.
+enum BwdPath { kBwdFused = 0, kBwdSplit = 1 };
+
+struct BwdPlan {
+    RowPlan rows;          // fused: the row-team plan
+    RowPlan sum_rows;      // split: the row plan of the row-sum pass (the forward's)
+    int path;
+    int64_t teams;         // fused: partial rows
+    int col_tiles;         // split
+    int tile_rows;         // split
+    int64_t row_blocks;    // split: partial rows
+    size_t rowpart_bytes;  // split: offset of the column partials in the workspace
+    size_t workspace;      // bytes either path needs (the larger of the two)
+};
+
+bool make_bwd_plan(const spr_desc& d, BwdPlan* plan);
+
+// Kernel launches of the backward for this plan (fused: rows, finalize;
+// split: rowsum, main, finalize).
+int bwd_num_launches(const BwdPlan& plan);
 
 hipError_t launch_fwd(const spr_desc& d, const RowPlan& plan, const FwdArgs& a, hipStream_t s);
 
-// Number of row teams (= fp32 partial rows) the backward uses for this desc.
+// Number of row teams (= fp32 partial rows) the fused backward uses.
 int64_t bwd_teams(const spr_desc& d, const RowPlan& plan);
-hipError_t launch_bwd(const spr_desc& d, const RowPlan& plan, const BwdArgs& a, hipStream_t s);
+// Runs launches [first, last) of the backward's sequence.
+hipError_t launch_bwd(const spr_desc& d, const BwdPlan& plan, const BwdArgs& a, hipStream_t s,
+                      int first, int last);
 
 }  // namespace spr

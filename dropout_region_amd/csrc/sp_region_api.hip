@@ -3,6 +3,8 @@
 // HIP call, so an invalid call launches nothing and touches no output.
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include "sp_plan.h"
 #include "sp_region.h"
@@ -53,6 +55,44 @@ bool make_row_plan(int io, int64_t h, PlanKind kind, RowPlan* plan) {
     p.rpw = 1;
     p.block = p.tpr;
     p.lb = best_lb;
+    *plan = p;
+    return true;
+}
+
+static size_t round256(uint64_t b) { return (size_t)((b + 255u) & ~(uint64_t)255u); }
+
+// Chooses the backward path: fused whenever its row team fits in registers
+// (at most two vectors per thread), split otherwise -- measured on MI355X,
+// the fused path is the faster one wherever it applies, even on shards where
+// its partial rows outweigh the split path's second read of dy and h.
+// SPR_BWD_PATH=fused|split asks for one path (tests check both).
+bool make_bwd_plan(const spr_desc& d, BwdPlan* plan) {
+    BwdPlan p{};
+    if (!make_row_plan(d.io, d.h, kPlanBackward, &p.rows)) return false;
+    if (!make_row_plan(d.io, d.h, kPlanForward, &p.sum_rows)) return false;
+    const int64_t rows = d.s_local * d.b;
+    const bool fused_ok = p.rows.vpt <= 2;
+    p.teams = bwd_teams(d, p.rows);
+
+    p.col_tiles = (p.rows.nvec + 63) / 64;
+    // About one 4-wave tile per CU, rows per tile a multiple of 16.
+    int64_t tr = rows * p.col_tiles / 256;
+    tr = tr / 16 * 16;
+    if (tr < 16) tr = 16;
+    const int64_t rows16 = (rows + 15) / 16 * 16;
+    if (tr > rows16) tr = rows16;
+    p.tile_rows = (int)tr;
+    p.row_blocks = (rows + tr - 1) / tr;
+    p.rowpart_bytes = round256((uint64_t)rows * 2u * sizeof(float));
+
+    const uint64_t fused_ws = (uint64_t)p.teams * 3u * (uint64_t)d.h * sizeof(float);
+    const uint64_t split_ws = p.rowpart_bytes + (uint64_t)p.row_blocks * 3u * (uint64_t)d.h * sizeof(float);
+    p.workspace = round256(fused_ws > split_ws ? fused_ws : split_ws);
+
+    p.path = fused_ok ? kBwdFused : kBwdSplit;
+    const char* force = getenv("SPR_BWD_PATH");
+    if (force && strcmp(force, "split") == 0) p.path = kBwdSplit;
+    if (force && strcmp(force, "fused") == 0 && fused_ok) p.path = kBwdFused;
     *plan = p;
     return true;
 }
@@ -116,11 +156,6 @@ spr_status check_desc(const spr_desc* d, RowPlan* plan, PlanKind kind) {
     return SPR_OK;
 }
 
-size_t workspace_bytes(const spr_desc* d, const RowPlan& plan) {
-    const uint64_t bytes = (uint64_t)bwd_teams(*d, plan) * 3u * (uint64_t)d->h * sizeof(float);
-    return (size_t)((bytes + 255u) & ~(uint64_t)255u);
-}
-
 }  // namespace
 
 extern "C" {
@@ -153,9 +188,10 @@ spr_status sp_region_activation_bytes(const spr_desc* d, uint64_t* saved_for_bwd
 }
 
 size_t sp_region_bwd_workspace_bytes(const spr_desc* d) {
-    RowPlan plan;
-    if (check_desc(d, &plan, kPlanBackward) != SPR_OK) return 0;
-    return workspace_bytes(d, plan);
+    RowPlan rp;
+    BwdPlan plan;
+    if (check_desc(d, &rp, kPlanBackward) != SPR_OK || !make_bwd_plan(*d, &plan)) return 0;
+    return plan.workspace;
 }
 
 spr_status sp_region_fwd(const spr_desc* d, const void* x, const float* bias,
@@ -207,14 +243,21 @@ spr_status sp_region_fwd(const spr_desc* d, const void* x, const float* bias,
     return launch_fwd(*d, plan, a, stream) == hipSuccess ? SPR_OK : SPR_ERR_HIP;
 }
 
-spr_status sp_region_bwd(const spr_desc* d, const void* dy, const void* dh_out, const void* h,
-                         const uint8_t* mask, const float* mean, const float* rstd,
-                         const float* gamma, void* dx_out, void* dres_out, float* dgamma_out,
-                         float* dbeta_out, float* dbias_out, void* workspace,
-                         size_t workspace_bytes_given, hipStream_t stream) {
-    RowPlan plan;
-    spr_status st = check_desc(d, &plan, kPlanBackward);
+}  // extern "C"
+
+namespace {
+
+// Every check of the backward, then the kernel arguments and plan.
+spr_status prepare_bwd(const spr_desc* d, const void* dy, const void* dh_out, const void* h,
+                       const uint8_t* mask, const float* mean, const float* rstd,
+                       const float* gamma, void* dx_out, void* dres_out, float* dgamma_out,
+                       float* dbeta_out, float* dbias_out, void* workspace,
+                       size_t workspace_bytes_given, BwdPlan* plan_out, BwdArgs* args_out) {
+    RowPlan rp;
+    spr_status st = check_desc(d, &rp, kPlanBackward);
     if (st != SPR_OK) return st;
+    BwdPlan plan;
+    if (!make_bwd_plan(*d, &plan)) return SPR_ERR_UNSUPPORTED;
     const bool ln = d->norm == SPR_LAYERNORM, drop = d->p > 0.0f;
     if (!dy || !h || !rstd || !gamma || !dx_out || !dres_out || !dgamma_out)
         return SPR_ERR_INVALID_ARG;
@@ -227,7 +270,7 @@ spr_status sp_region_bwd(const spr_desc* d, const void* dy, const void* dh_out, 
     if (!aligned(mask, 8) || !aligned(mean, 4) || !aligned(rstd, 4) || !aligned(dgamma_out, 4) ||
         !aligned(dbeta_out, 4) || !aligned(dbias_out, 4))
         return SPR_ERR_INVALID_ARG;
-    const size_t need = workspace_bytes(d, plan);
+    const size_t need = plan.workspace;
     if (!workspace || workspace_bytes_given < need || !aligned(workspace, 16))
         return SPR_ERR_WORKSPACE;
 
@@ -246,15 +289,64 @@ spr_status sp_region_bwd(const spr_desc* d, const void* dy, const void* dh_out, 
     BwdArgs a{};
     a.dy = dy; a.dh_out = dh_out; a.h = h; a.mask = mask; a.mean = mean; a.rstd = rstd;
     a.gamma = gamma; a.dx_out = dx_out; a.dres_out = dres_out;
-    a.partials = static_cast<float*>(workspace);
+    const bool split = plan.path == kBwdSplit;
+    a.rowpart = static_cast<float*>(workspace);
+    a.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                          (split ? plan.rowpart_bytes : 0));
     a.dgamma_out = dgamma_out; a.dbeta_out = dbeta_out; a.dbias_out = dbias_out;
     a.rows = rows;
     a.hidden = d->h;
     a.scale = (float)(1.0 / (1.0 - (double)d->p));
     a.inv_h = (float)(1.0 / (double)d->h);
-    a.nvec = plan.nvec;
-    a.teams = (int)bwd_teams(*d, plan);
-    return launch_bwd(*d, plan, a, stream) == hipSuccess ? SPR_OK : SPR_ERR_HIP;
+    a.nvec = plan.rows.nvec;
+    a.teams = (int)(split ? plan.row_blocks : plan.teams);
+    a.col_tiles = plan.col_tiles;
+    a.tile_rows = plan.tile_rows;
+    *plan_out = plan;
+    *args_out = a;
+    return SPR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+spr_status sp_region_bwd(const spr_desc* d, const void* dy, const void* dh_out, const void* h,
+                         const uint8_t* mask, const float* mean, const float* rstd,
+                         const float* gamma, void* dx_out, void* dres_out, float* dgamma_out,
+                         float* dbeta_out, float* dbias_out, void* workspace,
+                         size_t workspace_bytes_given, hipStream_t stream) {
+    BwdPlan plan;
+    BwdArgs a;
+    const spr_status st = prepare_bwd(d, dy, dh_out, h, mask, mean, rstd, gamma, dx_out, dres_out,
+                                      dgamma_out, dbeta_out, dbias_out, workspace,
+                                      workspace_bytes_given, &plan, &a);
+    if (st != SPR_OK) return st;
+    return launch_bwd(*d, plan, a, stream, 0, bwd_num_launches(plan)) == hipSuccess ? SPR_OK
+                                                                                    : SPR_ERR_HIP;
+}
+
+int sp_region_bwd_num_launches(const spr_desc* d) {
+    RowPlan rp;
+    BwdPlan plan;
+    if (check_desc(d, &rp, kPlanBackward) != SPR_OK || !make_bwd_plan(*d, &plan)) return 0;
+    return bwd_num_launches(plan);
+}
+
+spr_status sp_region_bwd_launch(const spr_desc* d, int index, const void* dy, const void* dh_out,
+                                const void* h, const uint8_t* mask, const float* mean,
+                                const float* rstd, const float* gamma, void* dx_out,
+                                void* dres_out, float* dgamma_out, float* dbeta_out,
+                                float* dbias_out, void* workspace, size_t workspace_bytes_given,
+                                hipStream_t stream) {
+    BwdPlan plan;
+    BwdArgs a;
+    const spr_status st = prepare_bwd(d, dy, dh_out, h, mask, mean, rstd, gamma, dx_out, dres_out,
+                                      dgamma_out, dbeta_out, dbias_out, workspace,
+                                      workspace_bytes_given, &plan, &a);
+    if (st != SPR_OK) return st;
+    if (index < 0 || index >= bwd_num_launches(plan)) return SPR_ERR_INVALID_ARG;
+    return launch_bwd(*d, plan, a, stream, index, index + 1) == hipSuccess ? SPR_OK : SPR_ERR_HIP;
 }
 
 }  // extern "C"

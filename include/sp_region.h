@@ -158,6 +158,25 @@ spr_status sp_region_bwd(const spr_desc* desc,
                          void* workspace, size_t workspace_bytes,
                          hipStream_t stream);
 
+/* The backward is a fixed sequence of kernel launches on `stream`: the row
+ * pass(es), then a fixed-order column finalize of the parameter gradients.
+ * sp_region_bwd runs the whole sequence.  These two let a caller run it one
+ * launch at a time -- to time each kernel with events on the stream, or to
+ * place the small finalize where it overlaps other work; launching indices
+ * 0 .. n-1 in order on one stream is exactly sp_region_bwd.  Same arguments
+ * and checks as sp_region_bwd.  sp_region_bwd_num_launches returns 0 for an
+ * invalid desc; sp_region_bwd_launch returns SPR_ERR_INVALID_ARG for an
+ * index outside 0 .. n-1. */
+int sp_region_bwd_num_launches(const spr_desc* desc);
+spr_status sp_region_bwd_launch(const spr_desc* desc, int index,
+                                const void* dy, const void* dh_out, const void* h,
+                                const uint8_t* mask, const float* mean, const float* rstd,
+                                const float* gamma,
+                                void* dx_out, void* dres_out,
+                                float* dgamma_out, float* dbeta_out, float* dbias_out,
+                                void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
 /* Bytes one forward call keeps (host arithmetic, no device access):
  *  saved_for_bwd   = h + mask (p > 0) + per-token statistics
  *  retained_output = y, the next block's input

@@ -148,11 +148,28 @@ def gpu_fwd(d, inp, with_bias=True, device="cuda:0"):
     return {k: to_host(v) for k, v in o.items()}
 
 
-def gpu_bwd(d, inp, saved, with_dh_out=False, want_dbias=True, device="cuda:0", repeat=1):
+def gpu_bwd(d, inp, saved, with_dh_out=False, want_dbias=True, device="cuda:0", repeat=1,
+            path=None):
     """Backward from `saved` (host arrays of h, mask, mean, rstd).  With
     repeat > 1 the call is made that many times into the same outputs and
-    workspace, and every result must be bit-identical."""
+    workspace, and every result must be bit-identical.  path = "fused" or
+    "split" asks the library for that backward path (SPR_BWD_PATH)."""
+    import os
     import dropout_region_amd as spr
+    old = os.environ.get("SPR_BWD_PATH")
+    if path is not None:
+        os.environ["SPR_BWD_PATH"] = path
+    try:
+        return _gpu_bwd(spr, d, inp, saved, with_dh_out, want_dbias, device, repeat)
+    finally:
+        if path is not None:
+            if old is None:
+                del os.environ["SPR_BWD_PATH"]
+            else:
+                os.environ["SPR_BWD_PATH"] = old
+
+
+def _gpu_bwd(spr, d, inp, saved, with_dh_out, want_dbias, device, repeat):
     io = d.io
     args = (to_device(inp["dy"], io, device),
             to_device(inp["dh_out"], io, device) if with_dh_out else None,

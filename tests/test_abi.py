@@ -30,6 +30,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["sp_region_fwd", "sp_region_bwd", "sp_region_bwd_workspace_bytes",
+                            "sp_region_bwd_num_launches", "sp_region_bwd_launch",
                             "sp_region_activation_bytes", "sp_region_status_string"])
 
 
@@ -98,6 +99,23 @@ def test_fwd_pointer_rules(L):
     bad = list(FWD_OK)
     bad[6] = FWD_OK[5]                           # y_out aliases h_out
     assert _fwd_raw(L, d, bad) == spr.SPR_ERR_INVALID_ARG
+
+
+def test_bwd_launch_count(L):
+    assert L.sp_region_bwd_num_launches(ctypes.byref(_good_desc())) == 2         # fused
+    assert L.sp_region_bwd_num_launches(ctypes.byref(_good_desc(h=25600))) == 3  # split
+    assert L.sp_region_bwd_num_launches(ctypes.byref(_good_desc(p=1.0))) == 0
+
+
+def test_bwd_launch_index_checked(L):
+    d = _good_desc()
+    need = L.sp_region_bwd_workspace_bytes(ctypes.byref(d))
+    ptrs = [A + i * 0x100000 for i in range(12)]
+    ptrs[1] = 0
+    for index in (-1, 2, 7):
+        assert L.sp_region_bwd_launch(ctypes.byref(d), index, *[ctypes.c_void_p(p) for p in ptrs],
+                                      ctypes.c_void_p(A + 0x4000000), ctypes.c_size_t(need),
+                                      None) == spr.SPR_ERR_INVALID_ARG
 
 
 def test_bwd_workspace_rules(L):

@@ -36,7 +36,10 @@ def descs(**kw):
     return spr.Desc(**kw), oracle.Desc(**kw)
 
 
-def run_case(name, kw, seed=0, with_bias=True, with_dh_out=False, want_dbias=True):
+def run_case(name, kw, seed=0, with_bias=True, with_dh_out=False, want_dbias=True,
+             paths=(None,)):
+    """paths: backward paths to check (None = the library's own choice,
+    "fused", "split")."""
     d, od = descs(**kw)
     _say(f"[case] {name}: {kw} bias={with_bias} dh_out={with_dh_out} dbias={want_dbias}")
     inp = make_inputs(d.rows, d.h, d.io, seed=seed, dh_out=with_dh_out)
@@ -44,10 +47,12 @@ def run_case(name, kw, seed=0, with_bias=True, with_dh_out=False, want_dbias=Tru
     got = P.gpu_fwd(d, inp, with_bias)
     P.check_fwd(got, want, d.io)
     wb = P.oracle_bwd(od, inp, want, with_dh_out, want_dbias)
-    gb = P.gpu_bwd(d, inp, want, with_dh_out, want_dbias, repeat=2)
-    P.check_bwd(gb, wb, d.io)
-    gc = P.gpu_bwd(d, inp, got, with_dh_out, want_dbias)
-    P.check_bwd(gc, wb, d.io)
+    for path in paths:
+        _say(f"[case] {name}: backward path {path or 'auto'}")
+        gb = P.gpu_bwd(d, inp, want, with_dh_out, want_dbias, repeat=2, path=path)
+        P.check_bwd(gb, wb, d.io)
+        gc = P.gpu_bwd(d, inp, got, with_dh_out, want_dbias, path=path)
+        P.check_bwd(gc, wb, d.io)
     return inp, got, gb
 
 
@@ -84,7 +89,8 @@ SMALL = {
 
 @pytest.mark.parametrize("name", sorted(SMALL))
 def test_small_shapes(name):
-    run_case(name, SMALL[name], seed=zlib.crc32(name.encode()) % 1000, with_dh_out=True)
+    run_case(name, SMALL[name], seed=zlib.crc32(name.encode()) % 1000, with_dh_out=True,
+             paths=(None, "fused", "split"))
 
 
 @pytest.mark.parametrize("with_bias,with_dh_out,want_dbias", [(False, False, True),
@@ -94,7 +100,7 @@ def test_small_shapes(name):
 def test_optional_arguments(with_bias, with_dh_out, want_dbias, io, norm):
     kw = base(s_local=6, b=2, h=6144 if io == BF16 else 1024, io=io, norm=norm)
     run_case(f"optional io={io} norm={norm}", kw, seed=3, with_bias=with_bias,
-             with_dh_out=with_dh_out, want_dbias=want_dbias)
+             with_dh_out=with_dh_out, want_dbias=want_dbias, paths=("fused", "split"))
 
 
 @pytest.mark.parametrize("io,h,t", [(F32, 256, 2), (BF16, 6144, 4), (BF16, 25600, 2)])
@@ -154,6 +160,33 @@ def test_workspace_and_argument_errors_leave_outputs_untouched():
     assert e.value.status == spr.SPR_ERR_WORKSPACE
 
 
+@pytest.mark.parametrize("path", ["fused", "split"])
+def test_launch_by_launch_equals_whole_backward(path, monkeypatch):
+    """Running the backward's launches one at a time on the stream gives the
+    same bits as sp_region_bwd."""
+    import torch
+    monkeypatch.setenv("SPR_BWD_PATH", path)
+    d, od = descs(**base(s_local=37, b=2, h=6144))
+    _say(f"[case] launch by launch, path {path}")
+    inp = make_inputs(d.rows, d.h, d.io, seed=4, dh_out=True)
+    saved = P.oracle_fwd(od, inp)
+    args = (P.to_device(inp["dy"], d.io), P.to_device(inp["dh_out"], d.io),
+            P.to_device(saved["h"], d.io), P.to_device(saved["mask"]), P.to_device(saved["mean"]),
+            P.to_device(saved["rstd"]), P.to_device(inp["gamma"]))
+    whole = spr.alloc_bwd_outputs(d, "cuda:0")
+    spr.sp_region_bwd(d, *args, whole["dx"], whole["dres"], whole["dgamma"], whole["dbeta"],
+                      whole["dbias"], whole["workspace"])
+    parts = spr.alloc_bwd_outputs(d, "cuda:0")
+    n = spr.sp_region_bwd_num_launches(d)
+    assert n == (2 if path == "fused" else 3)
+    for i in range(n):
+        spr.sp_region_bwd_launch(d, i, *args, parts["dx"], parts["dres"], parts["dgamma"],
+                                 parts["dbeta"], parts["dbias"], parts["workspace"])
+    torch.cuda.synchronize()
+    for k in ("dx", "dres", "dgamma", "dbeta", "dbias"):
+        P.exact(k, P.to_host(parts[k]), P.to_host(whole[k]))
+
+
 def test_outputs_stay_inside_their_buffers():
     """Every output is a view into a larger buffer whose guard bands hold a
     pattern; after fwd and bwd the guards are unchanged."""
@@ -207,7 +240,8 @@ def test_full_size_workload(name):
     """The workloads at their real shard shapes, in the launch configuration
     the benchmark times; every element is compared."""
     w = WORKLOADS[name]
-    run_case(name, _full_kw(w), seed=w.seed, with_dh_out=(w.norm == RMS))
+    run_case(name, _full_kw(w), seed=w.seed, with_dh_out=(w.norm == RMS),
+             paths=(None, "fused", "split"))
 
 
 def test_full_size_175b_layer_two_calls():
