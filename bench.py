@@ -118,8 +118,9 @@ def _profile_name(workload, what):
 
 def _short(name):
     """Readable kernel name: sp_region_fwd_kernel etc. (template arguments dropped)."""
-    for base in ("sp_region_fwd_kernel", "sp_region_bwd_rows_kernel", "sp_region_bwd_rowsum_kernel",
-                 "sp_region_bwd_main_kernel", "sp_region_bwd_finalize_kernel"):
+    for base in ("sp_region_fwd_kernel", "sp_region_fwd_stream_kernel", "sp_region_bwd_rows_kernel",
+                 "sp_region_bwd_rowsum_kernel", "sp_region_bwd_main_kernel",
+                 "sp_region_bwd_finalize_kernel"):
         if base in name:
             return base
     return name
@@ -284,22 +285,78 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = ev0.elapsed_time(ev1) / args.steps
 
-    # ---- timed region 2: HIP events around each kernel launch on the stream
-    # (the backward run one launch at a time -- the same launches in order)
+    # ---- timed region 2: each kernel alone.  A chunk of back-to-back
+    # launches of one kernel is captured in a HIP graph and replayed between
+    # two HIP events on the stream, so the host's launch rate does not show
+    # in a short kernel's time.  Kernel k runs over the buffer sets after
+    # kernel k-1 has run over all of them, so every launch reads what the
+    # launch before it in the sequence wrote for the same set (the backward
+    # launched one index at a time: the launches sp_region_bwd makes).
     nk = 1 + n_bwd
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        s = sets[i % nsets]
-        evs[i][0].record(stream)
-        fwd(s)
-        evs[i][1].record(stream)
-        for k in range(n_bwd):
-            spr.sp_region_bwd_launch(d, k, *bwd_args(s), stream)
-            evs[i][2 + k].record(stream)
-    torch.cuda.synchronize()
-    per_kernel_ms = np.array([[e[k].elapsed_time(e[k + 1]) for k in range(nk)] for e in evs])
+    chunk = 10
+    n_chunks = max(1, args.steps // chunk)
+    per_kernel_ms = np.zeros((n_chunks, nk))
+    cap_stream = torch.cuda.Stream()
+    for k in range(nk):
+        def launches():
+            for i in range(chunk):
+                s = sets[i % nsets]
+                if k == 0:
+                    spr.sp_region_fwd(d, s["x"], bias, s["res"], gamma, beta, s["h"], s["y"],
+                                      s["mask"], s["mean"], s["rstd"])
+                else:
+                    spr.sp_region_bwd_launch(d, k - 1, *bwd_args(s))
+        g = torch.cuda.CUDAGraph()
+        cap_stream.wait_stream(stream)
+        with torch.cuda.graph(g, stream=cap_stream):
+            launches()
+        stream.wait_stream(cap_stream)
+        g.replay()
+        torch.cuda.synchronize()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_chunks + 1)]
+        evs[0].record(stream)
+        for c in range(n_chunks):
+            g.replay()
+            evs[c + 1].record(stream)
+        torch.cuda.synchronize()
+        per_kernel_ms[:, k] = [evs[c].elapsed_time(evs[c + 1]) / chunk for c in range(n_chunks)]
+        del g
     kernel_us = per_kernel_ms.mean(axis=0) * 1e3
-    names = ["sp_region_fwd_kernel"] + (
+
+    # ---- layers of two calls (pre-attention and pre-MLP): call B's residual
+    # is call A's h, and call A's backward takes call B's dresidual as dh_out
+    layer = None
+    if w.calls_per_layer == 2:
+        def layer_step(sA, sB):
+            spr.sp_region_fwd(dA, sA["x"], bias, sA["res"], gamma, beta, sA["h"], sA["y"],
+                              sA["mask"], sA["mean"], sA["rstd"], stream)
+            spr.sp_region_fwd(dB, sB["x"], bias, sA["h"], gamma, beta, sB["h"], sB["y"],
+                              sB["mask"], sB["mean"], sB["rstd"], stream)
+            spr.sp_region_bwd(dB, *bwd_args(sB), stream)
+            spr.sp_region_bwd(dA, sA["dy"], sB["b_dres"], *bwd_args(sA)[2:], stream)
+        dA = d
+        dB = spr.Desc(**{**d.__dict__, "offset": 1})
+        pairs = [(sets[i], sets[(i + 1) % nsets]) for i in range(0, nsets, 2)]
+        for i in range(2):
+            layer_step(*pairs[i % len(pairs)])
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(args.steps):
+            layer_step(*pairs[i % len(pairs)])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        layer_ms = e0.elapsed_time(e1) / args.steps
+        fA, rA, gA = algorithmic_bytes(w, with_dh_out=True)
+        fB, rB, gB = algorithmic_bytes(w)
+        layer_bytes = fA + rA + gA + fB + rB + gB
+        layer = {"calls": 2, "ms_per_layer": round(layer_ms, 5),
+                 "tokens_per_s": round(w.rows / (layer_ms / 1e3), 1),
+                 "hbm_gbps": round(layer_bytes / (layer_ms / 1e3) / 1e9, 1),
+                 "algorithmic_bytes": layer_bytes}
+
+    # launch 0 is sp_region_fwd: its row kernel or its stream kernel
+    names = ["sp_region_fwd"] + (
         ["sp_region_bwd_rows_kernel", "sp_region_bwd_finalize_kernel"] if n_bwd == 2 else
         ["sp_region_bwd_rowsum_kernel", "sp_region_bwd_main_kernel", "sp_region_bwd_finalize_kernel"])
     fwd_b, bwd_rows_b, bwd_grad_b = algorithmic_bytes(w)
@@ -313,9 +370,11 @@ def main():
     achieved = alg[dom] / (kernel_us[dom] / 1e6) / 1e9
     traffic = load_traffic(w.name)
     dom_traffic = None
-    if traffic and names[dom] in traffic:
-        t = traffic[names[dom]]
-        dom_traffic = t["fetch_bytes"] + t["write_bytes"]
+    aliases = {"sp_region_fwd": ("sp_region_fwd_kernel", "sp_region_fwd_stream_kernel")}
+    for kname in aliases.get(names[dom], (names[dom],)):
+        if traffic and kname in traffic:
+            t = traffic[kname]
+            dom_traffic = t["fetch_bytes"] + t["write_bytes"]
     copy_gbps = copy_bandwidth(torch)
 
     out = {
@@ -333,6 +392,8 @@ def main():
         "kernels_us": {n: round(float(u), 2) for n, u in zip(names, kernel_us)},
         "kernels_us_p10_p90": {n: [round(float(np.percentile(per_kernel_ms[:, k], q)) * 1e3, 2)
                                    for q in (10, 90)] for k, n in enumerate(names)},
+        "kernel_timing": f"HIP events around replays of a HIP graph of {chunk} launches of one kernel",
+        "fwd_kernel": os.environ.get("SPR_FWD_PATH", "auto"),
         "algorithmic_bytes": {"fwd": fwd_b, "bwd": bwd_rows_b + bwd_grad_b},
         "wall_s_timed_region": round(wall, 4),
         "roofline": {"bound": "hbm", "kernel": names[dom], "achieved": round(achieved, 1),
@@ -340,6 +401,8 @@ def main():
                      "traffic": dom_traffic, "algorithmic_bytes_per_launch": alg[dom],
                      "launch_us": round(float(kernel_us[dom]), 2)},
     }
+    if layer is not None:
+        out["layer"] = layer
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w)

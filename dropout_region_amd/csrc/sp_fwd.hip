@@ -8,80 +8,39 @@
 //   mean/rstd of the rounded h, y = (h - mean) * rstd * gamma + beta (RMSNorm:
 //   y = h * rstd * gamma).
 // One pass over HBM: x and residual are read once, h, mask, y and the two
-// statistics written once; the row stays in registers between the two
-// reductions (mean, then the centred sum of squares).  Bias/gamma/beta are
-// re-read per row and come from L2.  h is bit-exact: u, v and h are each a
-// single fp32 operation rounded to nearest even (no contraction into FMA),
-// then rounded to the I/O type.
+// statistics written once; the row stays in registers from its load to its
+// last store.  Two kernels: the row kernel (one team per row, parameters
+// read per row from L2) and the stream kernel (a chip-filling grid walking
+// rows with the next row's loads in flight, parameters held in registers).
+// h is bit-exact: u, v and h are each a single fp32 operation rounded to
+// nearest even (no contraction into FMA), then rounded to the I/O type.
+#include <atomic>
+#include <cstdlib>
+#include <cstring>
+
 #include "sp_device.h"
 #include "sp_plan.h"
 
 namespace spr {
 
-// WAVE_ROWS: each wave owns one row (short rows, 4 rows per workgroup, no
-// LDS); otherwise the whole workgroup owns one row.  EXACT: the row is
-// exactly VPT vectors per thread, so no slot is idle.
-//
-// Every load is issued unconditionally (a ragged row's idle slots re-read its
-// last vector and are masked afterwards), so a thread has all its x and
-// residual vectors in flight at once; the dropout words, which need no
-// data, are computed while they arrive.  Statistics: each thread reduces
-// its own values to (count, mean, M2), then one Chan merge over the team.
-template <typename IO, int NORM, bool DROP, int VPT, bool WAVE_ROWS, int LB, bool EXACT>
-__global__ void __launch_bounds__(LB) sp_region_fwd_kernel(FwdArgs a) {
+// Pieces of one row's forward, shared by the two kernels below.  Thread
+// `tid` of the row's team owns vectors vc[k] = k*tpr + tid (ok[k] false for
+// the idle slots of a ragged row, which re-read the row's last vector and are
+// masked afterwards).
+
+// Dropout decisions, h = residual + dropout(x + bias) and its stores (h, and
+// the mask when p > 0); returns the thread's sum of its h values.  Element
+// (row, c) is element e = (row_base + row)*h + c of the full tensor; its
+// word is word e%4 of Philox block e/4.
+template <typename IO, bool DROP, int VPT>
+__device__ __forceinline__ float fwd_dropout_residual(const FwdArgs& a, int64_t row,
+                                                      const int (&vc)[VPT], const bool (&ok)[VPT],
+                                                      const uint4 (&xq)[VPT], const uint4 (&rq)[VPT],
+                                                      const float (&bb)[VPT][Vec<IO>::N],
+                                                      float (&hv)[VPT][Vec<IO>::N]) {
     constexpr int E = Vec<IO>::N;
     constexpr int MW = E / 4;                 // mask words per vector
-    __shared__ float red[48];
-
-    int tid, tpr, nwaves;
-    int64_t row;
-    if (WAVE_ROWS) {
-        tid = threadIdx.x & 63;
-        tpr = 64;
-        nwaves = 1;
-        row = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-    } else {
-        tid = threadIdx.x;
-        tpr = blockDim.x;
-        nwaves = blockDim.x >> 6;
-        row = blockIdx.x;
-    }
-    // Uniform per wave (WAVE_ROWS) or per workgroup: no barrier is skipped
-    // by part of a team.
-    if (row >= a.rows) return;
-
     const int64_t rbase = row * a.hidden;
-    const IO* xr = static_cast<const IO*>(a.x) + rbase;
-    const IO* rr = static_cast<const IO*>(a.residual) + rbase;
-
-    int vc[VPT];
-    bool ok[VPT];
-#pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-        const int vec = k * tpr + tid;
-        ok[k] = EXACT || vec < a.nvec;
-        vc[k] = ok[k] ? vec : a.nvec - 1;
-    }
-
-    uint4 xq[VPT], rq[VPT];
-#pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-        xq[k] = load_stream(xr + (int64_t)vc[k] * E);
-        rq[k] = load_stream(rr + (int64_t)vc[k] * E);
-    }
-    float bb[VPT][E];
-    if (a.bias) {
-#pragma unroll
-        for (int k = 0; k < VPT; ++k) load_params<E>(a.bias + (int64_t)vc[k] * E, bb[k]);
-    } else {
-#pragma unroll
-        for (int k = 0; k < VPT; ++k)
-#pragma unroll
-            for (int j = 0; j < E; ++j) bb[k][j] = 0.0f;
-    }
-
-    // Dropout decisions: element (row, c) is element e = (row_base+row)*h + c
-    // of the full tensor; its word is word e%4 of Philox block e/4.
     bool keep[VPT][E];
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
@@ -96,8 +55,6 @@ __global__ void __launch_bounds__(LB) sp_region_fwd_kernel(FwdArgs a) {
             for (int j = 0; j < E; ++j) keep[k][j] = true;   // p == 0: scale is exactly 1
         }
     }
-
-    float hv[VPT][E];
     float sum = 0.0f;
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
@@ -116,15 +73,18 @@ __global__ void __launch_bounds__(LB) sp_region_fwd_kernel(FwdArgs a) {
             }
         }
     }
+    return sum;
+}
 
-    float g[VPT][E], bt[VPT][E];
-#pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-        load_params<E>(a.gamma + (int64_t)vc[k] * E, g[k]);
-        if (NORM == SPR_LAYERNORM) load_params<E>(a.beta + (int64_t)vc[k] * E, bt[k]);
-    }
-
-    float mean = 0.0f, var;
+// The row's statistics over the team (one block reduction through `red`):
+// LayerNorm merges each thread's (count, mean, M2) (Chan et al.); RMSNorm
+// sums squares.  Returns mean (0 for RMSNorm) and rstd.
+template <int NORM, int VPT, int E>
+__device__ __forceinline__ void fwd_stats(const FwdArgs& a, const bool (&ok)[VPT],
+                                          const float (&hv)[VPT][E], float sum, float* red,
+                                          int nwaves, float& mean, float& rstd) {
+    float var;
+    mean = 0.0f;
     if (NORM == SPR_LAYERNORM) {
         float n = 0.0f;
 #pragma unroll
@@ -155,9 +115,20 @@ __global__ void __launch_bounds__(LB) sp_region_fwd_kernel(FwdArgs a) {
         }
         var = block_sum(sq, red, nwaves) * a.inv_h;     // mean square
     }
-    const float rstd = rsqrtf(var + a.eps);
-    const float shift = -mean * rstd;                   // xhat = h * rstd + shift
+    rstd = rsqrtf(var + a.eps);
+}
 
+// y = Norm(h) * gamma (+ beta) and the row's statistics.
+template <typename IO, int NORM, int VPT>
+__device__ __forceinline__ void fwd_store_y(const FwdArgs& a, int64_t row, int tid,
+                                            const int (&vc)[VPT], const bool (&ok)[VPT],
+                                            const float (&hv)[VPT][Vec<IO>::N],
+                                            const float (&g)[VPT][Vec<IO>::N],
+                                            const float (&bt)[VPT][Vec<IO>::N], float mean,
+                                            float rstd) {
+    constexpr int E = Vec<IO>::N;
+    const float shift = -mean * rstd;                   // xhat = h * rstd + shift
+    const int64_t rbase = row * a.hidden;
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
         if (ok[k]) {
@@ -173,6 +144,147 @@ __global__ void __launch_bounds__(LB) sp_region_fwd_kernel(FwdArgs a) {
     if (tid == 0) {
         if (NORM == SPR_LAYERNORM) a.mean_out[row] = mean;
         a.rstd_out[row] = rstd;
+    }
+}
+
+template <int VPT>
+__device__ __forceinline__ void row_slots(int tid, int tpr, int nvec, bool exact, int (&vc)[VPT],
+                                          bool (&ok)[VPT]) {
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+        const int vec = k * tpr + tid;
+        ok[k] = exact || vec < nvec;
+        vc[k] = ok[k] ? vec : nvec - 1;
+    }
+}
+
+template <typename IO, int VPT>
+__device__ __forceinline__ void load_x_res(const FwdArgs& a, int64_t row, const int (&vc)[VPT],
+                                           uint4 (&xq)[VPT], uint4 (&rq)[VPT]) {
+    constexpr int E = Vec<IO>::N;
+    const int64_t rbase = row * a.hidden;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+        xq[k] = load_stream(static_cast<const IO*>(a.x) + rbase + (int64_t)vc[k] * E);
+        rq[k] = load_stream(static_cast<const IO*>(a.residual) + rbase + (int64_t)vc[k] * E);
+    }
+}
+
+template <int VPT, int E>
+__device__ __forceinline__ void load_bias(const FwdArgs& a, const int (&vc)[VPT],
+                                          float (&bb)[VPT][E]) {
+    if (a.bias) {
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) load_params<E>(a.bias + (int64_t)vc[k] * E, bb[k]);
+    } else {
+#pragma unroll
+        for (int k = 0; k < VPT; ++k)
+#pragma unroll
+            for (int j = 0; j < E; ++j) bb[k][j] = 0.0f;
+    }
+}
+
+template <int NORM, int VPT, int E>
+__device__ __forceinline__ void load_affine(const FwdArgs& a, const int (&vc)[VPT],
+                                            float (&g)[VPT][E], float (&bt)[VPT][E]) {
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+        load_params<E>(a.gamma + (int64_t)vc[k] * E, g[k]);
+        if (NORM == SPR_LAYERNORM) load_params<E>(a.beta + (int64_t)vc[k] * E, bt[k]);
+    }
+}
+
+// Row kernel: one team per row.  WAVE_ROWS: each wave owns one row (short
+// rows, 4 rows per workgroup, no LDS); otherwise the whole workgroup owns
+// one row.  EXACT: the row is exactly VPT vectors per thread.
+//
+// Every load is issued unconditionally, so a thread has all its x and
+// residual vectors in flight at once; the dropout words, which need no
+// data, are computed while they arrive.  bias, gamma and beta come from L2.
+template <typename IO, int NORM, bool DROP, int VPT, bool WAVE_ROWS, int LB, bool EXACT>
+__global__ void __launch_bounds__(LB) sp_region_fwd_kernel(FwdArgs a) {
+    constexpr int E = Vec<IO>::N;
+    __shared__ float red[48];
+
+    int tid, tpr, nwaves;
+    int64_t row;
+    if (WAVE_ROWS) {
+        tid = threadIdx.x & 63;
+        tpr = 64;
+        nwaves = 1;
+        row = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    } else {
+        tid = threadIdx.x;
+        tpr = blockDim.x;
+        nwaves = blockDim.x >> 6;
+        row = blockIdx.x;
+    }
+    // Uniform per wave (WAVE_ROWS) or per workgroup: no barrier is skipped
+    // by part of a team.
+    if (row >= a.rows) return;
+
+    int vc[VPT];
+    bool ok[VPT];
+    row_slots<VPT>(tid, tpr, a.nvec, EXACT, vc, ok);
+    uint4 xq[VPT], rq[VPT];
+    load_x_res<IO, VPT>(a, row, vc, xq, rq);
+    float bb[VPT][E];
+    load_bias<VPT, E>(a, vc, bb);
+
+    float hv[VPT][E];
+    const float sum = fwd_dropout_residual<IO, DROP, VPT>(a, row, vc, ok, xq, rq, bb, hv);
+
+    float g[VPT][E], bt[VPT][E];
+    load_affine<NORM, VPT, E>(a, vc, g, bt);
+    float mean, rstd;
+    fwd_stats<NORM, VPT, E>(a, ok, hv, sum, red, nwaves, mean, rstd);
+    fwd_store_y<IO, NORM, VPT>(a, row, tid, vc, ok, hv, g, bt, mean, rstd);
+}
+
+// Stream kernel: a grid of G workgroups, about as many as fit on the chip at
+// once; workgroup b owns rows b, b + G, b + 2G, ...  bias, gamma and beta are
+// the same columns for every row, so they are loaded once and held; the next
+// row's x and residual are loaded before the current row is computed, so its
+// loads are in flight during the current row's arithmetic, reduction and
+// stores.  Two register sets alternate (A computes while B loads, then B
+// computes while A loads).  The LDS reduction slots alternate too, so a
+// row's reduction never overwrites a slot that a slower wave may still be
+// reading for the previous row.
+template <typename IO, int NORM, bool DROP, int VPT, int LB, bool EXACT>
+__global__ void __launch_bounds__(LB) sp_region_fwd_stream_kernel(FwdArgs a) {
+    constexpr int E = Vec<IO>::N;
+    __shared__ float red[2][48];
+    const int tid = threadIdx.x, tpr = blockDim.x, nwaves = blockDim.x >> 6;
+    const int64_t step = gridDim.x;
+
+    int vc[VPT];
+    bool ok[VPT];
+    row_slots<VPT>(tid, tpr, a.nvec, EXACT, vc, ok);
+
+    int64_t row = blockIdx.x;          // uniform over the workgroup
+    if (row >= a.rows) return;
+    uint4 xa[VPT], ra[VPT], xb[VPT], rb[VPT];
+    load_x_res<IO, VPT>(a, row, vc, xa, ra);
+    float bb[VPT][E], g[VPT][E], bt[VPT][E];
+    load_bias<VPT, E>(a, vc, bb);
+    load_affine<NORM, VPT, E>(a, vc, g, bt);
+
+    auto one_row = [&](int64_t r, const uint4 (&xq)[VPT], const uint4 (&rq)[VPT], float* slot) {
+        float hv[VPT][E];
+        const float sum = fwd_dropout_residual<IO, DROP, VPT>(a, r, vc, ok, xq, rq, bb, hv);
+        float mean, rstd;
+        fwd_stats<NORM, VPT, E>(a, ok, hv, sum, slot, nwaves, mean, rstd);
+        fwd_store_y<IO, NORM, VPT>(a, r, tid, vc, ok, hv, g, bt, mean, rstd);
+    };
+    for (;;) {
+        if (row + step < a.rows) load_x_res<IO, VPT>(a, row + step, vc, xb, rb);
+        one_row(row, xa, ra, red[0]);
+        row += step;
+        if (row >= a.rows) break;
+        if (row + step < a.rows) load_x_res<IO, VPT>(a, row + step, vc, xa, ra);
+        one_row(row, xb, rb, red[1]);
+        row += step;
+        if (row >= a.rows) break;
     }
 }
 
@@ -222,7 +334,110 @@ static hipError_t fwd_by_norm(const spr_desc& d, const RowPlan& p, const FwdArgs
                                    : fwd_by_drop<IO, SPR_RMSNORM>(d, p, a, s);
 }
 
+// ---------------------------------------------------------------- stream kernel dispatch
+static hipError_t cu_count(int* cus) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (*cus < 1) *cus = 1;
+    return e;
+}
+
+// Workgroups of the stream kernel: per CU, enough for at least 8 waves (as
+// many as fit, if fewer), then trimmed so that every workgroup gets the same
+// number of rows (or one fewer).
+template <typename K>
+static hipError_t stream_grid(K kernel, int block, int64_t rows, int cus, int64_t* grid) {
+    static std::atomic<int> fit{0};       // workgroups of this kernel that fit on a CU
+    int occ = fit.load(std::memory_order_relaxed);
+    if (occ == 0) {
+        const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, block, 0);
+        if (e != hipSuccess) return e;
+        if (occ < 1) occ = 1;
+        fit.store(occ, std::memory_order_relaxed);
+    }
+    const int waves = (block + 63) / 64;
+    int per_cu = (8 + waves - 1) / waves;
+    if (per_cu > occ) per_cu = occ;
+    const int64_t cap = (int64_t)per_cu * cus;
+    const int64_t per_wg = (rows + cap - 1) / cap;
+    *grid = (rows + per_wg - 1) / per_wg;
+    return hipSuccess;
+}
+
+template <typename IO, int NORM, bool DROP, int V, bool EXACT>
+static hipError_t fwd_stream_launch(const RowPlan& p, const FwdArgs& a, hipStream_t s) {
+    constexpr int LB = stream_bound(Vec<IO>::N, V);
+    auto kernel = sp_region_fwd_stream_kernel<IO, NORM, DROP, V, LB, EXACT>;
+    int cus = 0;
+    hipError_t e = cu_count(&cus);
+    if (e != hipSuccess) return e;
+    int64_t grid = 0;
+    e = stream_grid(kernel, p.block, a.rows, cus, &grid);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3((unsigned)p.block), 0, s, a);
+    return hipGetLastError();
+}
+
+template <typename IO, int NORM, bool DROP, bool EXACT>
+static hipError_t fwd_stream_by_vpt(const RowPlan& p, const FwdArgs& a, hipStream_t s) {
+    if constexpr (Vec<IO>::N == 8) {
+        switch (p.vpt) {
+            case 1: return fwd_stream_launch<IO, NORM, DROP, 1, EXACT>(p, a, s);
+            case 2: return fwd_stream_launch<IO, NORM, DROP, 2, EXACT>(p, a, s);
+            default: return hipErrorInvalidValue;
+        }
+    } else {
+        switch (p.vpt) {
+            case 1: return fwd_stream_launch<IO, NORM, DROP, 1, EXACT>(p, a, s);
+            case 2: return fwd_stream_launch<IO, NORM, DROP, 2, EXACT>(p, a, s);
+            case 3: return fwd_stream_launch<IO, NORM, DROP, 3, EXACT>(p, a, s);
+            case 4: return fwd_stream_launch<IO, NORM, DROP, 4, EXACT>(p, a, s);
+            default: return hipErrorInvalidValue;
+        }
+    }
+}
+
+template <typename IO, int NORM>
+static hipError_t fwd_stream_by_mode(const spr_desc& d, const RowPlan& p, const FwdArgs& a,
+                                     hipStream_t s) {
+    const bool exact = p.nvec == p.vpt * p.tpr;
+    if (d.p > 0.0f)
+        return exact ? fwd_stream_by_vpt<IO, NORM, true, true>(p, a, s)
+                     : fwd_stream_by_vpt<IO, NORM, true, false>(p, a, s);
+    return exact ? fwd_stream_by_vpt<IO, NORM, false, true>(p, a, s)
+                 : fwd_stream_by_vpt<IO, NORM, false, false>(p, a, s);
+}
+
+template <typename IO>
+static hipError_t fwd_stream_by_norm(const spr_desc& d, const RowPlan& p, const FwdArgs& a,
+                                     hipStream_t s) {
+    return d.norm == SPR_LAYERNORM ? fwd_stream_by_mode<IO, SPR_LAYERNORM>(d, p, a, s)
+                                   : fwd_stream_by_mode<IO, SPR_RMSNORM>(d, p, a, s);
+}
+
+// The stream kernel where its plan exists (at most 16 elements per thread,
+// so bias, gamma and beta fit in registers next to two row buffers) and the
+// shard has more than four rows per CU; else the row kernel.  Measured on
+// MI355X: with up to four rows per CU every row's workgroup is resident at
+// once and the row kernel is faster; with more, the stream kernel's overlap
+// of the next row's loads with the current row's work wins.
+// SPR_FWD_PATH=rows|stream asks for one kernel (tests check both).
 hipError_t launch_fwd(const spr_desc& d, const RowPlan& p, const FwdArgs& a, hipStream_t s) {
+    RowPlan sp;
+    const char* force = getenv("SPR_FWD_PATH");
+    bool stream = make_stream_plan(d.io, d.h, &sp);
+    if (stream && !(force && strcmp(force, "stream") == 0)) {
+        int cus = 0;
+        const hipError_t e = cu_count(&cus);
+        if (e != hipSuccess) return e;
+        stream = a.rows > 4 * (int64_t)cus;
+    }
+    if (force && strcmp(force, "rows") == 0) stream = false;
+    if (stream)
+        return d.io == SPR_BF16 ? fwd_stream_by_norm<__bf16>(d, sp, a, s)
+                                : fwd_stream_by_norm<float>(d, sp, a, s);
     return d.io == SPR_BF16 ? fwd_by_norm<__bf16>(d, p, a, s) : fwd_by_norm<float>(d, p, a, s);
 }
 

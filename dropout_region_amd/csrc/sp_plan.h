@@ -38,6 +38,17 @@ static constexpr VptBound kBwdCombos[] = {{1, 1024}, {2, 768}, {3, 512}, {4, 512
 
 enum PlanKind { kPlanForward, kPlanBackward };
 
+// Launch bound of the forward's stream kernel for VPT vectors of E
+// elements per thread: 1024 threads (128 VGPRs) up to 8 elements, 768 (168)
+// up to 12, else 512 (256).
+constexpr int stream_bound(int e, int vpt) {
+    return e * vpt <= 8 ? 1024 : (e * vpt <= 12 ? 768 : 512);
+}
+// Row plan of the forward's stream kernel (one workgroup per row team, at
+// most 16 elements per thread); false where it does not apply (short rows,
+// which go one wave per row, and wide rows).
+bool make_stream_plan(int io, int64_t h, RowPlan* plan);
+
 // Picks a row plan for h; false if h is unsupported.  The forward prefers
 // about four vectors per thread, the backward (which keeps three column
 // accumulators per element) as few as possible.

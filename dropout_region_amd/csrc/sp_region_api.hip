@@ -59,6 +59,39 @@ bool make_row_plan(int io, int64_t h, PlanKind kind, RowPlan* plan) {
     return true;
 }
 
+bool make_stream_plan(int io, int64_t h, RowPlan* plan) {
+    const int epv = (io == SPR_BF16) ? 8 : 4;
+    if (h <= 0 || h % epv != 0) return false;
+    const int64_t nvec = h / epv;
+    if (nvec <= 4 * 64) return false;        // one wave per row instead
+    // Most vectors per thread first (more bytes in flight per thread); the
+    // first split with no idle slot, else the one with the fewest.
+    const int max_vpt = 16 / epv;
+    int best_vpt = 0;
+    int64_t best_tpr = 0, best_waste = INT64_MAX;
+    for (int v = max_vpt; v >= 1; --v) {
+        const int64_t tpr = ((nvec + v - 1) / v + 63) / 64 * 64;
+        if (tpr > stream_bound(epv, v)) continue;
+        const int64_t waste = tpr * v - nvec;
+        if (waste < best_waste) {
+            best_waste = waste;
+            best_vpt = v;
+            best_tpr = tpr;
+        }
+    }
+    if (best_vpt == 0) return false;
+    RowPlan p{};
+    p.epv = epv;
+    p.nvec = (int)nvec;
+    p.vpt = best_vpt;
+    p.tpr = (int)best_tpr;
+    p.rpw = 1;
+    p.block = p.tpr;
+    p.lb = stream_bound(epv, best_vpt);
+    *plan = p;
+    return true;
+}
+
 static size_t round256(uint64_t b) { return (size_t)((b + 255u) & ~(uint64_t)255u); }
 
 // Chooses the backward path: fused whenever its row team fits in registers

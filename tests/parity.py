@@ -11,6 +11,9 @@ accumulation on the GPU and float64 in the oracle:
   dgamma, dbeta, dbias (fp32): max|a - b| / max|b| <= 1e-4
 ulp_bf16(b) = 2^(floor(log2 |b|) - 7), the spacing of bfloat16 at b.
 """
+import contextlib
+import os
+
 import numpy as np
 
 F32, BF16 = 0, 1
@@ -138,13 +141,33 @@ def oracle_bwd(od, inp, saved, with_dh_out=False, want_dbias=True):
                       want_dbias=want_dbias)
 
 
-def gpu_fwd(d, inp, with_bias=True, device="cuda:0"):
+@contextlib.contextmanager
+def _env(name, value):
+    """Sets environment variable `name` to `value` (None: leave it alone)
+    for the duration of the block."""
+    old = os.environ.get(name)
+    if value is not None:
+        os.environ[name] = value
+    try:
+        yield
+    finally:
+        if value is not None:
+            if old is None:
+                del os.environ[name]
+            else:
+                os.environ[name] = old
+
+
+def gpu_fwd(d, inp, with_bias=True, device="cuda:0", path=None):
+    """Forward on the GPU; path = "rows" or "stream" asks the library for
+    that forward kernel (SPR_FWD_PATH), None for its own choice."""
     import dropout_region_amd as spr
     io = d.io
-    o = spr.fwd(d, to_device(inp["x"], io, device),
-                to_device(inp["bias"], device=device) if with_bias else None,
-                to_device(inp["residual"], io, device), to_device(inp["gamma"], device=device),
-                to_device(inp["beta"], device=device) if d.norm == 0 else None)
+    with _env("SPR_FWD_PATH", path):
+        o = spr.fwd(d, to_device(inp["x"], io, device),
+                    to_device(inp["bias"], device=device) if with_bias else None,
+                    to_device(inp["residual"], io, device), to_device(inp["gamma"], device=device),
+                    to_device(inp["beta"], device=device) if d.norm == 0 else None)
     return {k: to_host(v) for k, v in o.items()}
 
 
@@ -154,19 +177,9 @@ def gpu_bwd(d, inp, saved, with_dh_out=False, want_dbias=True, device="cuda:0", 
     repeat > 1 the call is made that many times into the same outputs and
     workspace, and every result must be bit-identical.  path = "fused" or
     "split" asks the library for that backward path (SPR_BWD_PATH)."""
-    import os
     import dropout_region_amd as spr
-    old = os.environ.get("SPR_BWD_PATH")
-    if path is not None:
-        os.environ["SPR_BWD_PATH"] = path
-    try:
+    with _env("SPR_BWD_PATH", path):
         return _gpu_bwd(spr, d, inp, saved, with_dh_out, want_dbias, device, repeat)
-    finally:
-        if path is not None:
-            if old is None:
-                del os.environ["SPR_BWD_PATH"]
-            else:
-                os.environ["SPR_BWD_PATH"] = old
 
 
 def _gpu_bwd(spr, d, inp, saved, with_dh_out, want_dbias, device, repeat):

@@ -37,15 +37,17 @@ def descs(**kw):
 
 
 def run_case(name, kw, seed=0, with_bias=True, with_dh_out=False, want_dbias=True,
-             paths=(None,)):
+             paths=(None,), fwd_paths=(None,)):
     """paths: backward paths to check (None = the library's own choice,
-    "fused", "split")."""
+    "fused", "split"); fwd_paths: forward kernels (None, "rows", "stream")."""
     d, od = descs(**kw)
     _say(f"[case] {name}: {kw} bias={with_bias} dh_out={with_dh_out} dbias={want_dbias}")
     inp = make_inputs(d.rows, d.h, d.io, seed=seed, dh_out=with_dh_out)
     want = P.oracle_fwd(od, inp, with_bias)
-    got = P.gpu_fwd(d, inp, with_bias)
-    P.check_fwd(got, want, d.io)
+    for fpath in fwd_paths:
+        _say(f"[case] {name}: forward kernel {fpath or 'auto'}")
+        got = P.gpu_fwd(d, inp, with_bias, path=fpath)
+        P.check_fwd(got, want, d.io)
     wb = P.oracle_bwd(od, inp, want, with_dh_out, want_dbias)
     for path in paths:
         _say(f"[case] {name}: backward path {path or 'auto'}")
@@ -84,13 +86,15 @@ SMALL = {
     "bf16_ln_high_counter_words": base(s_local=2, b=1, h=32768, shard_index=2**20 - 1,
                                        t=2**20, seed=2**64 - 1, offset=2**63 + 5),
     "bf16_ln_p0.9": base(s_local=4, b=2, h=6144, p=0.9),
+    "fp32_ln_h8192_1100_rows": base(s_local=550, b=2, h=8192, io=F32),
+    "bf16_rms_h12288_1500_rows": base(s_local=500, b=3, h=12288, norm=RMS, p=0.2),
 }
 
 
 @pytest.mark.parametrize("name", sorted(SMALL))
 def test_small_shapes(name):
     run_case(name, SMALL[name], seed=zlib.crc32(name.encode()) % 1000, with_dh_out=True,
-             paths=(None, "fused", "split"))
+             paths=(None, "fused", "split"), fwd_paths=(None, "rows", "stream"))
 
 
 @pytest.mark.parametrize("with_bias,with_dh_out,want_dbias", [(False, False, True),
