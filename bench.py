@@ -45,7 +45,7 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(w, with_bias=True, with_dh_out=False):
+def algorithmic_bytes(w, with_bias=True, with_dh_out=False, mask_stored=True):
     """Bytes the region must move per call (re-reads, partial sums and
     spills excluded).
     forward : read x, residual (2 es/elem), write h, y (2 es/elem), mask
@@ -57,7 +57,7 @@ def algorithmic_bytes(w, with_bias=True, with_dh_out=False):
     pass moves, bwd_grads the three gradient rows the finalize writes."""
     E, N, H = w.elems, w.rows, w.h
     es = 2 if w.io == 1 else 4
-    m = 1 if w.p > 0 else 0
+    m = 1 if w.p > 0 and mask_stored else 0
     ln = w.norm == 0
     n_par = (1 if with_bias else 0) + 1 + (1 if ln else 0)
     n_stat = 2 if ln else 1
@@ -192,6 +192,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--min-set-bytes", type=float, default=1.0, help="GiB of rotated buffers")
+    ap.add_argument("--no-mask", action="store_true",
+                    help="mask-free region: the forward stores no mask, the backward "
+                         "regenerates the dropout decisions")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--stats-summary", metavar="TRACE_DIR")
     ap.add_argument("--command", default="", help="command recorded in a summary")
@@ -229,11 +232,13 @@ def main():
         od = oracle.Desc(**{k: getattr(d, k) for k in ("s_local", "b", "h", "shard_index", "t",
                                                          "io", "norm", "p", "eps", "seed",
                                                          "offset")})
-        got = P.gpu_fwd(d, inp)
+        got = P.gpu_fwd(d, inp, store_mask=not args.no_mask)
         rows = sorted({0, 1, w.rows // 2, w.rows - 1})
         for r in rows:
             sl, st = slice(r * w.h, (r + 1) * w.h), slice(r, r + 1)
             want = P.oracle_fwd(od, inp, rows=(r, r + 1))
+            if args.no_mask:
+                want["mask"] = None
             P.check_fwd({k: (v[sl] if k in ("h", "y", "mask") else v[st]) if v is not None else None
                          for k, v in got.items()}, want, w.io)
         print(f"[bench] parity ok on rows {rows}", file=sys.stderr, flush=True)
@@ -250,7 +255,7 @@ def main():
     sets = []
     for _ in range(nsets):
         s = {"x": x0.clone(), "res": r0.clone(), "dy": dy0.clone()}
-        s.update(spr.alloc_fwd_outputs(d, dev))
+        s.update(spr.alloc_fwd_outputs(d, dev, store_mask=not args.no_mask))
         s.update({("b_" + k): v for k, v in spr.alloc_bwd_outputs(d, dev).items()})
         sets.append(s)
     stream = torch.cuda.current_stream()
@@ -347,8 +352,8 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         layer_ms = e0.elapsed_time(e1) / args.steps
-        fA, rA, gA = algorithmic_bytes(w, with_dh_out=True)
-        fB, rB, gB = algorithmic_bytes(w)
+        fA, rA, gA = algorithmic_bytes(w, with_dh_out=True, mask_stored=not args.no_mask)
+        fB, rB, gB = algorithmic_bytes(w, mask_stored=not args.no_mask)
         layer_bytes = fA + rA + gA + fB + rB + gB
         layer = {"calls": 2, "ms_per_layer": round(layer_ms, 5),
                  "tokens_per_s": round(w.rows / (layer_ms / 1e3), 1),
@@ -359,7 +364,7 @@ def main():
     names = ["sp_region_fwd"] + (
         ["sp_region_bwd_rows_kernel", "sp_region_bwd_finalize_kernel"] if n_bwd == 2 else
         ["sp_region_bwd_rowsum_kernel", "sp_region_bwd_main_kernel", "sp_region_bwd_finalize_kernel"])
-    fwd_b, bwd_rows_b, bwd_grad_b = algorithmic_bytes(w)
+    fwd_b, bwd_rows_b, bwd_grad_b = algorithmic_bytes(w, mask_stored=not args.no_mask)
     # algorithmic bytes of each launch (the split path's row-sum pass only re-reads)
     alg = [fwd_b] + ([bwd_rows_b, bwd_grad_b] if n_bwd == 2 else [0, bwd_rows_b, bwd_grad_b])
 
@@ -385,7 +390,9 @@ def main():
         "config": {"workload": w.name, "shard": [w.s_local, w.b, w.h], "t": w.t,
                    "norm": "layernorm" if w.norm == 0 else "rmsnorm", "p": w.p, "eps": w.eps,
                    "io": "bf16" if w.io == 1 else "fp32", "params_and_stats": "fp32",
-                   "tokens_per_step": w.rows, "buffer_sets": nsets},
+                   "tokens_per_step": w.rows, "buffer_sets": nsets,
+                   "mask": ("regenerated in the backward" if args.no_mask else "stored uint8")
+                   if w.p > 0 else "none (p = 0)"},
         "hbm_gbps": round(gbps, 1), "hbm_frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4),
         "copy_gbps": round(copy_gbps, 1), "frac_of_copy": round(gbps / copy_gbps, 4),
         "bwd_path": os.environ.get("SPR_BWD_PATH", "auto"),

@@ -193,13 +193,14 @@ def sp_region_bwd_launch(d, index, dy, dh_out, h, mask, mean, rstd, gamma, dx_ou
 
 
 # ------------------------------------------------------------ allocation helpers
-def alloc_fwd_outputs(d, device):
-    """torch.empty outputs of sp_region_fwd: h, y, mask, mean, rstd."""
+def alloc_fwd_outputs(d, device, store_mask=True):
+    """torch.empty outputs of sp_region_fwd: h, y, mask, mean, rstd.  With
+    store_mask=False there is no mask (the backward regenerates it)."""
     import torch
     N, H, io = d.rows, d.h, _io_dtype(d)
     e = lambda n, dt: torch.empty(n, dtype=dt, device=device)
     return {"h": e(N * H, io), "y": e(N * H, io),
-            "mask": e(N * H, torch.uint8) if d.p > 0 else None,
+            "mask": e(N * H, torch.uint8) if d.p > 0 and store_mask else None,
             "mean": e(N, torch.float32) if d.norm == SPR_LAYERNORM else None,
             "rstd": e(N, torch.float32)}
 
@@ -216,9 +217,9 @@ def alloc_bwd_outputs(d, device, want_dbias=True):
             "workspace": torch.zeros(ws, dtype=torch.uint8, device=device)}
 
 
-def fwd(d, x, bias, residual, gamma, beta, stream=None):
+def fwd(d, x, bias, residual, gamma, beta, stream=None, store_mask=True):
     """Allocates the outputs and runs sp_region_fwd; returns them as a dict."""
-    o = alloc_fwd_outputs(d, x.device)
+    o = alloc_fwd_outputs(d, x.device, store_mask)
     sp_region_fwd(d, x, bias, residual, gamma, beta, o["h"], o["y"], o["mask"], o["mean"],
                   o["rstd"], stream)
     return o

@@ -30,7 +30,7 @@ struct RowIn {
     float mu, rs;
 };
 
-template <typename IO, int NORM, bool DROP, int VPT, bool WAVE_ROWS, int LB>
+template <typename IO, int NORM, int DROP, int VPT, bool WAVE_ROWS, int LB>
 __global__ void __launch_bounds__(LB) sp_region_bwd_rows_kernel(BwdArgs a) {
     // Prefetching the next row doubles the row's registers; wide rows
     // (more than two vectors per thread) load each row when they reach it.
@@ -80,7 +80,7 @@ __global__ void __launch_bounds__(LB) sp_region_bwd_rows_kernel(BwdArgs a) {
             const int64_t off = rbase + (int64_t)vc[k] * E;
             in.h[k] = load_stream(static_cast<const IO*>(a.h) + off);
             in.dy[k] = load_stream(static_cast<const IO*>(a.dy) + off);
-            if (DROP) {
+            if (DROP == kDropMask) {
 #pragma unroll
                 for (int w = 0; w < MW; ++w)
                     in.mask[k][w] = __builtin_nontemporal_load(
@@ -106,6 +106,17 @@ __global__ void __launch_bounds__(LB) sp_region_bwd_rows_kernel(BwdArgs a) {
             if (next < a.rows) load_row(next, nxt);
         } else {
             load_row(row, cur);
+        }
+
+        // Regenerated dropout: the row's keep bits, drawn while the row's
+        // loads are in flight.
+        uint32_t kbits[VPT];
+        if (DROP == kDropRegen) {
+#pragma unroll
+            for (int k = 0; k < VPT; ++k)
+                kbits[k] = keep_bits<E>((a.row_base + (uint64_t)row) * (uint64_t)a.hidden +
+                                            (uint64_t)vc[k] * E,
+                                        a.off_lo, a.off_hi, a.key_lo, a.key_hi, a.thr);
         }
 
         V hv[VPT], dyv[VPT];
@@ -134,9 +145,11 @@ __global__ void __launch_bounds__(LB) sp_region_bwd_rows_kernel(BwdArgs a) {
             V dho, dres, dx;
             if (a.dh_out) dho.set(cur.dho[k]);
             uint32_t kb = 0xffu;
-            if (DROP) {
+            if (DROP == kDropMask) {
                 kb = MaskBytes<4>::from_word(cur.mask[k][0]);
                 if (MW == 2) kb |= MaskBytes<4>::from_word(cur.mask[k][MW - 1]) << 4;
+            } else if (DROP == kDropRegen) {
+                kb = kbits[k];
             }
 #pragma unroll
             for (int j = 0; j < E; ++j) {
@@ -145,7 +158,8 @@ __global__ void __launch_bounds__(LB) sp_region_bwd_rows_kernel(BwdArgs a) {
                 float dh = (NORM == SPR_LAYERNORM) ? cur.rs * (g - mg - xh * mgx)
                                                    : cur.rs * (g - xh * mgx);
                 if (a.dh_out) dh += dho.v[j];
-                const float dxu = DROP ? (((kb >> j) & 1u) ? dh * a.scale : 0.0f) : dh;
+                const float dxu =
+                    DROP != kDropNone ? (((kb >> j) & 1u) ? dh * a.scale : 0.0f) : dh;
                 dres.v[j] = dh;
                 dx.v[j] = dxu;
                 if (ok[k]) {
@@ -337,7 +351,7 @@ struct TileIn {
     float2 rsum[U];
 };
 
-template <typename IO, int NORM, bool DROP>
+template <typename IO, int NORM, int DROP>
 __global__ void __launch_bounds__(256) sp_region_bwd_main_kernel(BwdArgs a) {
     using V = Vec<IO>;
     constexpr int E = V::N, U = kSplitUnroll, MW = E / 4;
@@ -364,7 +378,7 @@ __global__ void __launch_bounds__(256) sp_region_bwd_main_kernel(BwdArgs a) {
             const int64_t off = rc * a.hidden + (int64_t)vcl * E;
             in.h[u] = load_stream(static_cast<const IO*>(a.h) + off);
             in.dy[u] = load_stream(static_cast<const IO*>(a.dy) + off);
-            if (DROP) {
+            if (DROP == kDropMask) {
 #pragma unroll
                 for (int w = 0; w < MW; ++w)
                     in.mask[u][w] = __builtin_nontemporal_load(
@@ -395,9 +409,13 @@ __global__ void __launch_bounds__(256) sp_region_bwd_main_kernel(BwdArgs a) {
             dv.set(cur.dy[u]);
             if (a.dh_out) dho.set(cur.dho[u]);
             uint32_t kb = 0xffu;
-            if (DROP) {
+            if (DROP == kDropMask) {
                 kb = MaskBytes<4>::from_word(cur.mask[u][0]);
                 if (MW == 2) kb |= MaskBytes<4>::from_word(cur.mask[u][MW - 1]) << 4;
+            } else if (DROP == kDropRegen) {
+                kb = keep_bits<E>((a.row_base + (uint64_t)row) * (uint64_t)a.hidden +
+                                      (uint64_t)vcl * E,
+                                  a.off_lo, a.off_hi, a.key_lo, a.key_hi, a.thr);
             }
 #pragma unroll
             for (int j = 0; j < E; ++j) {
@@ -406,7 +424,8 @@ __global__ void __launch_bounds__(256) sp_region_bwd_main_kernel(BwdArgs a) {
                 float dh = (NORM == SPR_LAYERNORM) ? rs * (g - mg - xh * mgx)
                                                    : rs * (g - xh * mgx);
                 if (a.dh_out) dh += dho.v[j];
-                const float dxu = DROP ? (((kb >> j) & 1u) ? dh * a.scale : 0.0f) : dh;
+                const float dxu =
+                    DROP != kDropNone ? (((kb >> j) & 1u) ? dh * a.scale : 0.0f) : dh;
                 dres.v[j] = dh;
                 dx.v[j] = dxu;
                 if (ok && rok) {
@@ -438,7 +457,7 @@ int64_t bwd_teams(const spr_desc& d, const RowPlan& p) {
     return ((want + p.rpw - 1) / p.rpw) * p.rpw;
 }
 
-template <typename IO, int NORM, bool DROP, bool WR>
+template <typename IO, int NORM, int DROP, bool WR>
 static hipError_t bwd_by_vpt(const RowPlan& p, const BwdArgs& a, hipStream_t s) {
     const dim3 g((unsigned)(a.teams / p.rpw)), b((unsigned)p.block);
 #define SPR_BWD_CASE(V, L)                                                                       \
@@ -469,7 +488,7 @@ static hipError_t launch_finalize(const BwdArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <typename IO, int NORM, bool DROP>
+template <typename IO, int NORM, int DROP>
 static hipError_t bwd_by_mode(const RowPlan& p, const BwdArgs& a, hipStream_t s) {
     return p.rpw > 1 ? bwd_by_vpt<IO, NORM, DROP, true>(p, a, s)
                      : bwd_by_vpt<IO, NORM, DROP, false>(p, a, s);
@@ -511,13 +530,24 @@ static hipError_t split_rowsum(const BwdPlan& p, const BwdArgs& a, hipStream_t s
                  : rowsum_by_vpt<IO, NORM, false, false>(rp, a, s);
 }
 
+static int drop_mode(const spr_desc& d, const BwdArgs& a) {
+    if (!(d.p > 0.0f)) return kDropNone;
+    return a.mask ? kDropMask : kDropRegen;
+}
+
 template <typename IO, int NORM>
 static hipError_t split_main(const spr_desc& d, const BwdPlan& p, const BwdArgs& a, hipStream_t s) {
     const dim3 g((unsigned)p.col_tiles, (unsigned)p.row_blocks), b(256);
-    if (d.p > 0.0f)
-        hipLaunchKernelGGL((sp_region_bwd_main_kernel<IO, NORM, true>), g, b, 0, s, a);
-    else
-        hipLaunchKernelGGL((sp_region_bwd_main_kernel<IO, NORM, false>), g, b, 0, s, a);
+    switch (drop_mode(d, a)) {
+        case kDropMask:
+            hipLaunchKernelGGL((sp_region_bwd_main_kernel<IO, NORM, kDropMask>), g, b, 0, s, a);
+            break;
+        case kDropRegen:
+            hipLaunchKernelGGL((sp_region_bwd_main_kernel<IO, NORM, kDropRegen>), g, b, 0, s, a);
+            break;
+        default:
+            hipLaunchKernelGGL((sp_region_bwd_main_kernel<IO, NORM, kDropNone>), g, b, 0, s, a);
+    }
     return hipGetLastError();
 }
 
@@ -529,8 +559,13 @@ static hipError_t bwd_one(const spr_desc& d, const BwdPlan& p, const BwdArgs& a,
         if (index == 1) return split_main<IO, NORM>(d, p, a, s);
         return launch_finalize(a, s);
     }
-    if (index == 0) return d.p > 0.0f ? bwd_by_mode<IO, NORM, true>(p.rows, a, s)
-                                      : bwd_by_mode<IO, NORM, false>(p.rows, a, s);
+    if (index == 0) {
+        switch (drop_mode(d, a)) {
+            case kDropMask: return bwd_by_mode<IO, NORM, kDropMask>(p.rows, a, s);
+            case kDropRegen: return bwd_by_mode<IO, NORM, kDropRegen>(p.rows, a, s);
+            default: return bwd_by_mode<IO, NORM, kDropNone>(p.rows, a, s);
+        }
+    }
     return launch_finalize(a, s);
 }
 

@@ -58,6 +58,23 @@ __device__ __forceinline__ void keep4(uint64_t blk, uint32_t off_lo, uint32_t of
 }
 
 // Mask word of 4 keep decisions: byte j is 1 when element j is kept.
+// Keep decisions of the E consecutive elements from global element e0 (a
+// multiple of 4) as bits: bit j set = element e0 + j kept.  The same words
+// the forward drew (the backward regenerates them instead of reading a mask).
+template <int E>
+__device__ __forceinline__ uint32_t keep_bits(uint64_t e0, uint32_t off_lo, uint32_t off_hi,
+                                              uint32_t key_lo, uint32_t key_hi, uint32_t thr) {
+    uint32_t kb = 0;
+#pragma unroll
+    for (int q = 0; q < E / 4; ++q) {
+        bool k4[4];
+        keep4((e0 >> 2) + q, off_lo, off_hi, key_lo, key_hi, thr, k4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) kb |= (k4[j] ? 1u : 0u) << (4 * q + j);
+    }
+    return kb;
+}
+
 __device__ __forceinline__ uint32_t mask_word(const bool* keep) {
     return (keep[0] ? 1u : 0u) | (keep[1] ? 1u << 8 : 0u) | (keep[2] ? 1u << 16 : 0u) |
            (keep[3] ? 1u << 24 : 0u);

@@ -65,7 +65,7 @@ __device__ __forceinline__ float fwd_dropout_residual(const FwdArgs& a, int64_t 
             for (int j = 0; j < E; ++j) sum += hv[k][j];
             const int64_t off = rbase + (int64_t)vc[k] * E;
             store_stream(static_cast<IO*>(a.h_out) + off, hw);
-            if (DROP) {
+            if (DROP && a.mask_out) {         // no mask stored: the backward regenerates it
 #pragma unroll
                 for (int q = 0; q < MW; ++q)
                     __builtin_nontemporal_store(mask_word(&keep[k][4 * q]),

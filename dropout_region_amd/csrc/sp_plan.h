@@ -38,6 +38,11 @@ static constexpr VptBound kBwdCombos[] = {{1, 1024}, {2, 768}, {3, 512}, {4, 512
 
 enum PlanKind { kPlanForward, kPlanBackward };
 
+// How the backward learns the dropout decisions: none (p == 0), from the
+// stored mask, or regenerated from the counter-based generator (the forward
+// stored no mask).
+enum DropMode { kDropNone = 0, kDropMask = 1, kDropRegen = 2 };
+
 // Launch bound of the forward's stream kernel for VPT vectors of E
 // elements per thread: 1024 threads (128 VGPRs) up to 8 elements, 768 (168)
 // up to 12, else 512 (256).
@@ -93,6 +98,9 @@ struct BwdArgs {
     float* dbias_out;
     int64_t rows;
     int64_t hidden;
+    uint64_t row_base;     // shard_index * N (regenerated dropout only)
+    uint32_t key_lo, key_hi, off_lo, off_hi;
+    uint32_t thr;
     float scale;
     float inv_h;
     int nvec;

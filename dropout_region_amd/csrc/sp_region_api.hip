@@ -59,6 +59,21 @@ bool make_row_plan(int io, int64_t h, PlanKind kind, RowPlan* plan) {
     return true;
 }
 
+// The dropout's generator key and counter words, threshold and scale, as
+// both directions use them.  Element (r, c) of the shard is element
+// e = (shard_index*N + r)*h + c of the full tensor.
+template <typename Args>
+static void set_dropout(const spr_desc& d, int64_t rows, Args* a) {
+    a->row_base = (uint64_t)d.shard_index * (uint64_t)rows;
+    a->key_lo = (uint32_t)d.seed;
+    a->key_hi = (uint32_t)(d.seed >> 32);
+    a->off_lo = (uint32_t)d.offset;
+    a->off_hi = (uint32_t)(d.offset >> 32);
+    // keep iff word >= floor(p * 2^32); p * 2^32 is exact in double
+    a->thr = (uint32_t)floor((double)d.p * 4294967296.0);
+    a->scale = (float)(1.0 / (1.0 - (double)d.p));
+}
+
 bool make_stream_plan(int io, int64_t h, RowPlan* plan) {
     const int epv = (io == SPR_BF16) ? 8 : 4;
     if (h <= 0 || h % epv != 0) return false;
@@ -237,7 +252,6 @@ spr_status sp_region_fwd(const spr_desc* d, const void* x, const float* bias,
     const bool ln = d->norm == SPR_LAYERNORM, drop = d->p > 0.0f;
     if (!x || !residual || !gamma || !h_out || !y_out || !rstd_out) return SPR_ERR_INVALID_ARG;
     if (ln != (beta != nullptr) || ln != (mean_out != nullptr)) return SPR_ERR_INVALID_ARG;
-    if (drop && !mask_out) return SPR_ERR_INVALID_ARG;
     if (!drop) mask_out = nullptr;                                   // ignored at p == 0
     const void* io16[] = {x, residual, h_out, y_out};
     for (const void* p : io16)
@@ -262,14 +276,7 @@ spr_status sp_region_fwd(const spr_desc* d, const void* x, const float* bias,
     a.rstd_out = rstd_out;
     a.rows = rows;
     a.hidden = d->h;
-    a.row_base = (uint64_t)d->shard_index * (uint64_t)rows;
-    a.key_lo = (uint32_t)d->seed;
-    a.key_hi = (uint32_t)(d->seed >> 32);
-    a.off_lo = (uint32_t)d->offset;
-    a.off_hi = (uint32_t)(d->offset >> 32);
-    // keep iff word >= floor(p * 2^32); p * 2^32 is exact in double
-    a.thr = (uint32_t)floor((double)d->p * 4294967296.0);
-    a.scale = (float)(1.0 / (1.0 - (double)d->p));
+    set_dropout(*d, rows, &a);
     a.inv_h = (float)(1.0 / (double)d->h);
     a.eps = d->eps;
     a.nvec = plan.nvec;
@@ -295,8 +302,7 @@ spr_status prepare_bwd(const spr_desc* d, const void* dy, const void* dh_out, co
     if (!dy || !h || !rstd || !gamma || !dx_out || !dres_out || !dgamma_out)
         return SPR_ERR_INVALID_ARG;
     if (ln != (mean != nullptr) || ln != (dbeta_out != nullptr)) return SPR_ERR_INVALID_ARG;
-    if (drop && !mask) return SPR_ERR_INVALID_ARG;
-    if (!drop) mask = nullptr;
+    if (!drop) mask = nullptr;          // p > 0 without a mask: regenerated
     const void* io16[] = {dy, dh_out, h, dx_out, dres_out, gamma};
     for (const void* p : io16)
         if (!aligned(p, 16)) return SPR_ERR_INVALID_ARG;
@@ -329,7 +335,7 @@ spr_status prepare_bwd(const spr_desc* d, const void* dy, const void* dh_out, co
     a.dgamma_out = dgamma_out; a.dbeta_out = dbeta_out; a.dbias_out = dbias_out;
     a.rows = rows;
     a.hidden = d->h;
-    a.scale = (float)(1.0 / (1.0 - (double)d->p));
+    set_dropout(*d, rows, &a);
     a.inv_h = (float)(1.0 / (double)d->h);
     a.nvec = plan.rows.nvec;
     a.teams = (int)(split ? plan.row_blocks : plan.teams);

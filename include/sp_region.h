@@ -112,8 +112,15 @@ typedef struct {
  *  h_out    [N,h] io   residual + dropout(x + bias): the next residual and
  *                      the norm input kept for the backward
  *  y_out    [N,h] io   Norm(h): the input of the next tensor-parallel block
- *  mask_out [N,h] u8   1 = kept; required when p > 0; ignored (may be NULL)
- *                      when p == 0
+ *  mask_out [N,h] u8   1 = kept; ignored (may be NULL) when p == 0.  With
+ *                      p > 0 it may also be NULL: then no mask is stored
+ *                      and the backward regenerates the decisions from the
+ *                      same generator words (pass mask = NULL there too);
+ *                      this keeps N*h bytes fewer per call for extra
+ *                      arithmetic in the backward (a mask-free region, the
+ *                      trade-off the pages' accounting of the masks invites:
+ *                      "Sequence parallel math", "What tensor parallelism
+ *                      leaves replicated")
  *  mean_out [N]  fp32  LayerNorm: required; RMSNorm: must be NULL
  *  rstd_out [N]  fp32  1/sqrt(var + eps) (LayerNorm) or 1/sqrt(mean(h^2)+eps)
  * h_out and mask_out are bit-exact functions of the inputs; y and the
@@ -134,8 +141,11 @@ size_t sp_region_bwd_workspace_bytes(const spr_desc* desc);
  *  dy          [N,h] io   gradient of y
  *  dh_out      [N,h] io   gradient reaching h from outside the region (the
  *                         next block's residual branch); may be NULL (zero)
- *  h, mask, mean, rstd    as written by sp_region_fwd (mask and mean may be
- *                         NULL when p == 0, resp. for RMSNorm)
+ *  h, mask, mean, rstd    as written by sp_region_fwd (mean is NULL for
+ *                         RMSNorm; mask is NULL when p == 0, and with p > 0
+ *                         NULL means: regenerate the forward's decisions
+ *                         from desc's seed, offset, shard_index and t --
+ *                         the desc must then be the forward's)
  *  gamma       [h]  fp32
  *  dx_out      [N,h] io   gradient of x
  *  dres_out    [N,h] io   gradient of residual (= gradient of h)
@@ -178,7 +188,8 @@ spr_status sp_region_bwd_launch(const spr_desc* desc, int index,
                                 hipStream_t stream);
 
 /* Bytes one forward call keeps (host arithmetic, no device access):
- *  saved_for_bwd   = h + mask (p > 0) + per-token statistics
+ *  saved_for_bwd   = h + mask (p > 0, stored) + per-token statistics
+ *                    (a forward without a mask keeps N*h bytes fewer)
  *  retained_output = y, the next block's input
  * With bf16 I/O, a one-byte mask and two calls per layer (before attention
  * and before the MLP) this is 10*s*b*h/t bytes plus the statistics: the

@@ -158,16 +158,18 @@ def _env(name, value):
                 os.environ[name] = old
 
 
-def gpu_fwd(d, inp, with_bias=True, device="cuda:0", path=None):
+def gpu_fwd(d, inp, with_bias=True, device="cuda:0", path=None, store_mask=True):
     """Forward on the GPU; path = "rows" or "stream" asks the library for
-    that forward kernel (SPR_FWD_PATH), None for its own choice."""
+    that forward kernel (SPR_FWD_PATH), None for its own choice.
+    store_mask=False: no mask is stored (the backward regenerates it)."""
     import dropout_region_amd as spr
     io = d.io
     with _env("SPR_FWD_PATH", path):
         o = spr.fwd(d, to_device(inp["x"], io, device),
                     to_device(inp["bias"], device=device) if with_bias else None,
                     to_device(inp["residual"], io, device), to_device(inp["gamma"], device=device),
-                    to_device(inp["beta"], device=device) if d.norm == 0 else None)
+                    to_device(inp["beta"], device=device) if d.norm == 0 else None,
+                    store_mask=store_mask)
     return {k: to_host(v) for k, v in o.items()}
 
 

@@ -86,7 +86,10 @@ def test_fwd_pointer_rules(L):
     bad[0] = A + 8                               # x misaligned
     assert _fwd_raw(L, d, bad) == spr.SPR_ERR_INVALID_ARG
     bad = list(FWD_OK)
-    bad[7] = 0                                   # mask missing with p > 0
+    bad[7] = A + 0x600004                        # mask misaligned (8-byte words)
+    assert _fwd_raw(L, d, bad) == spr.SPR_ERR_INVALID_ARG
+    bad = list(FWD_OK)
+    bad[9] = 0                                   # rstd missing
     assert _fwd_raw(L, d, bad) == spr.SPR_ERR_INVALID_ARG
     bad = list(FWD_OK)
     bad[4] = 0                                   # beta missing for LayerNorm

@@ -97,6 +97,41 @@ def test_small_shapes(name):
              paths=(None, "fused", "split"), fwd_paths=(None, "rows", "stream"))
 
 
+# The mask-free region: the forward stores no mask and the backward
+# regenerates the decisions from the same generator words.
+MASK_FREE = {
+    "bf16_ln_h6144_fused": (base(s_local=40, b=2, h=6144, shard_index=3, t=8), "fused"),
+    "bf16_ln_h6144_split": (base(s_local=40, b=2, h=6144, shard_index=3, t=8), "split"),
+    "bf16_ln_h25600_split": (base(s_local=3, b=2, h=25600, shard_index=1, t=4), None),
+    "bf16_rms_h1000_wave_rows": (base(s_local=37, b=1, h=1000, norm=RMS, eps=1e-6), None),
+    "fp32_ln_h3076_ragged": (base(s_local=6, b=2, h=3076, io=F32, p=0.3), None),
+    "bf16_ln_h8192_1100_rows_stream": (base(s_local=1100, b=1, h=8192, offset=7), None),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MASK_FREE))
+def test_mask_free_region(name):
+    kw, path = MASK_FREE[name]
+    d, od = descs(**kw)
+    _say(f"[case] mask-free {name}: {kw} bwd path {path or 'auto'}")
+    inp = make_inputs(d.rows, d.h, d.io, seed=zlib.crc32(name.encode()) % 1000, dh_out=True)
+    want = P.oracle_fwd(od, inp)
+    with_mask = P.gpu_fwd(d, inp)
+    no_mask = P.gpu_fwd(d, inp, store_mask=False)
+    assert no_mask["mask"] is None
+    P.check_fwd(dict(no_mask, mask=with_mask["mask"]), want, d.io)
+    for k in ("h", "y", "mean", "rstd"):
+        if want[k] is not None:
+            P.exact(f"{k} (no mask stored vs stored)", no_mask[k], with_mask[k])
+    wb = P.oracle_bwd(od, inp, want, True, True)
+    regen = P.gpu_bwd(d, inp, dict(want, mask=None), with_dh_out=True, repeat=2, path=path)
+    P.check_bwd(regen, wb, d.io)
+    stored = P.gpu_bwd(d, inp, want, with_dh_out=True, path=path)
+    for k in ("dx", "dres", "dgamma", "dbeta", "dbias"):
+        if stored.get(k) is not None:
+            P.exact(f"{k} (regenerated vs stored mask)", regen[k], stored[k])
+
+
 @pytest.mark.parametrize("with_bias,with_dh_out,want_dbias", [(False, False, True),
                                                               (True, False, False),
                                                               (False, True, False)])
