@@ -83,6 +83,8 @@ def load(path):
     L.spo_f32_to_bf16.restype = ctypes.c_uint16
     L.spo_bf16_to_f32.argtypes = [ctypes.c_uint16]
     L.spo_bf16_to_f32.restype = ctypes.c_float
+    L.spo_reduce_parts.argtypes = [D, ctypes.c_int, P, P]
+    L.spo_reduce_parts.restype = ctypes.c_int
     L.spo_fwd.argtypes = [D, I64, I64] + [P] * 10
     L.spo_fwd.restype = ctypes.c_int
     L.spo_bwd.argtypes = [D, I64, I64] + [P] * 12
@@ -149,6 +151,21 @@ def bf16_to_f32(bits):
 
 
 # ---------------------------------------------------------------- region
+def reduce_parts(d, parts, L=None):
+    """x = round_io(parts[0] + parts[1] + ... in that order, fp32 adds).
+    parts: array of nparts * N * h I/O elements ([nparts][N][h])."""
+    L = L or lib()
+    io = _io_dtype(d)
+    n = d.rows * d.h
+    parts = np.ascontiguousarray(parts, dtype=io).ravel()
+    if parts.size % n != 0 or parts.size == 0:
+        raise ValueError("parts must hold nparts * N * h elements")
+    x = np.empty(n, io)
+    if L.spo_reduce_parts(ctypes.byref(d.c()), parts.size // n, _ptr(parts), _ptr(x)) != 0:
+        raise ValueError("spo_reduce_parts rejected its arguments")
+    return x
+
+
 def fwd(d, x, bias, residual, gamma, beta, rows=None, L=None):
     """Forward over rows [r0, r1) (default: the whole shard).  x and residual
     hold exactly those rows.  Returns dict h, y, mask, mean, rstd."""

@@ -244,6 +244,22 @@ static int ptr_rules_fwd(const spo_desc* d, const void* beta, const void* mean_o
 /* ------------------------------------------------------------------------ */
 /* Forward                                                                   */
 /* ------------------------------------------------------------------------ */
+/* Reduce-scatter prologue                                                   */
+/* ------------------------------------------------------------------------ */
+int spo_reduce_parts(const spo_desc* d, int nparts, const void* parts, void* x_out)
+{
+    if (!d || nparts < 1 || !parts || !x_out) return -1;
+    const int64_t n = rows_of(d) * d->h;
+    for (int64_t i = 0; i < n; ++i) {
+        float acc = load_io(d->io, parts, i);                       /* rank 0 */
+        for (int p = 1; p < nparts; ++p)
+            acc = acc + load_io(d->io, parts, (int64_t)p * n + i);   /* fp32 add, rank order */
+        store_io(d->io, x_out, i, acc);                              /* one rounding */
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 int spo_fwd(const spo_desc* d, int64_t r0, int64_t r1,
             const void* x, const float* bias, const void* residual,
             const float* gamma, const float* beta,

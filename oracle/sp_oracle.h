@@ -66,6 +66,22 @@ float    spo_dropout_scale(float p);
 uint16_t spo_f32_to_bf16(float f);
 float    spo_bf16_to_f32(uint16_t b);
 
+/* Reduce-scatter prologue of the region: x = round_io(sum over p of
+ * parts[p]) for every element of the shard, the parts added in rank order
+ * p = 0, 1, ..., nparts-1, each add one fp32 operation, then one rounding to
+ * the I/O type.  parts is [nparts][N][h] and x_out [N][h], both in the I/O
+ * type (N = s_local*b).  After the row-parallel linear each rank holds a
+ * partial sum of the block's output; the reduce-scatter that replaces the
+ * all-reduce under sequence parallelism hands rank i the sum over ranks of
+ * its own tokens' rows ("Tensor and sequence parallelism -- explained with
+ * pictures", section "Add Sequence parallelism"; "SP: Partition Activations
+ * Alongside TP", section "Connect SP and TP across a layer").  The order and
+ * the single rounding are this library's reading.  Returns 0, or -1 for
+ * nparts < 1 or a NULL pointer.
+ * Parity: pinned (identity at nparts = 1, exact integer sums, a case whose
+ * result depends on the order, bf16 ties of the final rounding). */
+int spo_reduce_parts(const spo_desc* d, int nparts, const void* parts, void* x_out);
+
 /* Forward over rows [r0, r1) of the shard.  Every per-row array (x, residual,
  * h_out, y_out, mask_out, mean_out, rstd_out) starts at row r0: element (r, c)
  * lives at index (r - r0) * h + c, and r only enters the global index.

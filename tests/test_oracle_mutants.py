@@ -63,6 +63,14 @@ MUTANTS = {
                        "double dhv = dh[c];"),
     "exact_dgamma_uses_g": ("dgamma_out[c] += dy[i] * xhat[c];",
                             "dgamma_out[c] += dy[i] * gamma[c] * xhat[c];"),
+    # reduce-scatter prologue
+    "reduce_reversed_order": ("float acc = load_io(d->io, parts, i);                       /* rank 0 */\n"
+                              "        for (int p = 1; p < nparts; ++p)",
+                              "float acc = load_io(d->io, parts, (int64_t)(nparts - 1) * n + i);\n"
+                              "        for (int p = nparts - 2; p >= 0; --p)"),
+    "reduce_rounds_each_add": ("acc = acc + load_io(d->io, parts, (int64_t)p * n + i);",
+                               "acc = store_io(d->io, x_out, i, acc + load_io(d->io, parts, (int64_t)p * n + i));"),
+    "reduce_drops_last_part": ("for (int p = 1; p < nparts; ++p)", "for (int p = 1; p < nparts - 1; ++p)"),
     # accounting
     "mask_counted_as_bf16": ("uint64_t mask_bytes = (d->p > 0.0f) ? E : 0u;",
                              "uint64_t mask_bytes = (d->p > 0.0f) ? 2u * E : 0u;"),
@@ -73,7 +81,14 @@ MUTANTS = {
 def _checks(L, philox):
     """Pin checks, each a callable raising on failure (all run against L)."""
     from tests import test_oracle_accounting as A
+    from tests import test_oracle_rs as S
     c = [
+        lambda: S.test_one_part_is_the_identity(L, BF16),
+        lambda: S.test_integer_parts_sum_exactly(L, F32, 8),
+        lambda: S.test_integer_parts_sum_exactly(L, BF16, 4),
+        lambda: S.test_parts_are_added_in_rank_order(L, F32),
+        lambda: S.test_parts_are_added_in_rank_order(L, BF16),
+        lambda: S.test_bf16_final_rounding_is_one_rne(L),
         lambda: G.test_philox_block_matches_torch_engine(L, philox),
         lambda: G.test_dropout_word_selects_word_e_mod_4_of_block_e_div_4(L, philox),
         lambda: G.test_mask_matches_library_words_and_global_index(L, philox),
