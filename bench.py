@@ -45,10 +45,11 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(w, with_bias=True, with_dh_out=False, mask_stored=True):
+def algorithmic_bytes(w, with_bias=True, with_dh_out=False, mask_stored=True, x_parts=1):
     """Bytes the region must move per call (re-reads, partial sums and
     spills excluded).
-    forward : read x, residual (2 es/elem), write h, y (2 es/elem), mask
+    forward : read x (x_parts slabs of it with the reduce-scatter
+              prologue), residual (es/elem each), write h, y (2 es/elem), mask
               (1 B/elem when p > 0), read bias/gamma/beta, write mean/rstd
     backward: read dy, h (2 es/elem), mask (1 B/elem), [dh_out] (es/elem),
               write dx, dres (2 es/elem), read gamma and the stats, write
@@ -61,7 +62,7 @@ def algorithmic_bytes(w, with_bias=True, with_dh_out=False, mask_stored=True):
     ln = w.norm == 0
     n_par = (1 if with_bias else 0) + 1 + (1 if ln else 0)
     n_stat = 2 if ln else 1
-    fwd = E * (4 * es + m) + n_par * H * 4 + n_stat * N * 4
+    fwd = E * ((x_parts + 3) * es + m) + n_par * H * 4 + n_stat * N * 4
     n_grad = 1 + (1 if ln else 0) + 1
     bwd_rows = E * (4 * es + m + (es if with_dh_out else 0)) + n_stat * N * 4 + H * 4
     return fwd, bwd_rows, n_grad * H * 4
@@ -192,6 +193,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--min-set-bytes", type=float, default=1.0, help="GiB of rotated buffers")
+    ap.add_argument("--rs-parts", type=int, default=0,
+                    help="forward with the reduce-scatter prologue over this many partial "
+                         "slabs (sp_region_fwd_rs); 0 = the plain forward")
     ap.add_argument("--no-mask", action="store_true",
                     help="mask-free region: the forward stores no mask, the backward "
                          "regenerates the dropout decisions")
@@ -225,6 +229,11 @@ def main():
     print(f"[bench] workload {w.name}: shard [{w.s_local}, {w.b}, {w.h}] N={w.rows} "
           f"on {torch.cuda.get_device_name(0)}", file=sys.stderr, flush=True)
     inp = make_inputs(w.rows, w.h, w.io, seed=w.seed)
+    K = args.rs_parts
+    parts_host = None
+    if K:
+        from sp_inputs import make_parts
+        parts_host = make_parts(w.rows, w.h, w.io, K, seed=w.seed)
 
     # ---- parity first: sampled rows against the oracle
     if not args.no_parity:
@@ -232,11 +241,16 @@ def main():
         od = oracle.Desc(**{k: getattr(d, k) for k in ("s_local", "b", "h", "shard_index", "t",
                                                          "io", "norm", "p", "eps", "seed",
                                                          "offset")})
-        got = P.gpu_fwd(d, inp, store_mask=not args.no_mask)
+        if K:
+            ref_inp = dict(inp, x=oracle.reduce_parts(od, parts_host))
+            got = P.gpu_fwd_rs(d, inp, parts_host, K)
+        else:
+            ref_inp = inp
+            got = P.gpu_fwd(d, inp, store_mask=not args.no_mask)
         rows = sorted({0, 1, w.rows // 2, w.rows - 1})
         for r in rows:
             sl, st = slice(r * w.h, (r + 1) * w.h), slice(r, r + 1)
-            want = P.oracle_fwd(od, inp, rows=(r, r + 1))
+            want = P.oracle_fwd(od, ref_inp, rows=(r, r + 1))
             if args.no_mask:
                 want["mask"] = None
             P.check_fwd({k: (v[sl] if k in ("h", "y", "mask") else v[st]) if v is not None else None
@@ -246,24 +260,31 @@ def main():
     # ---- device buffers: rotate sets so consecutive steps miss the MALL
     es = 2 if w.io == 1 else 4
     x0 = P.to_device(inp["x"], w.io)
+    parts0 = P.to_device(parts_host.ravel(), w.io) if K else None
     r0 = P.to_device(inp["residual"], w.io)
     dy0 = P.to_device(inp["dy"], w.io)
     bias, gamma = P.to_device(inp["bias"]), P.to_device(inp["gamma"])
     beta = P.to_device(inp["beta"]) if w.norm == 0 else None
-    set_bytes = w.elems * (7 * es + 1)
+    set_bytes = w.elems * ((7 + K) * es + 1)
     nsets = max(2, int(np.ceil(args.min_set_bytes * (1 << 30) / set_bytes)))
     sets = []
     for _ in range(nsets):
         s = {"x": x0.clone(), "res": r0.clone(), "dy": dy0.clone()}
+        if K:
+            s["parts"] = parts0.clone()
         s.update(spr.alloc_fwd_outputs(d, dev, store_mask=not args.no_mask))
         s.update({("b_" + k): v for k, v in spr.alloc_bwd_outputs(d, dev).items()})
         sets.append(s)
     stream = torch.cuda.current_stream()
     n_bwd = spr.sp_region_bwd_num_launches(d)
 
-    def fwd(s):
-        spr.sp_region_fwd(d, s["x"], bias, s["res"], gamma, beta, s["h"], s["y"], s["mask"],
-                          s["mean"], s["rstd"], stream)
+    def fwd(s, stream=stream):
+        if K:
+            spr.sp_region_fwd_rs(d, s["parts"], K, bias, s["res"], gamma, beta, s["h"], s["y"],
+                                 s["mask"], s["mean"], s["rstd"], stream)
+        else:
+            spr.sp_region_fwd(d, s["x"], bias, s["res"], gamma, beta, s["h"], s["y"], s["mask"],
+                              s["mean"], s["rstd"], stream)
 
     def bwd_args(s):
         return (s["dy"], None, s["h"], s["mask"], s["mean"], s["rstd"], gamma, s["b_dx"],
@@ -307,8 +328,7 @@ def main():
             for i in range(chunk):
                 s = sets[i % nsets]
                 if k == 0:
-                    spr.sp_region_fwd(d, s["x"], bias, s["res"], gamma, beta, s["h"], s["y"],
-                                      s["mask"], s["mean"], s["rstd"])
+                    fwd(s, stream=None)          # the capture stream
                 else:
                     spr.sp_region_bwd_launch(d, k - 1, *bwd_args(s))
         g = torch.cuda.CUDAGraph()
@@ -327,6 +347,35 @@ def main():
         per_kernel_ms[:, k] = [evs[c].elapsed_time(evs[c + 1]) / chunk for c in range(n_chunks)]
         del g
     kernel_us = per_kernel_ms.mean(axis=0) * 1e3
+
+    # ---- the reduce-scatter prologue against its unfused form (torch's sum of
+    # the slabs, fp32 accumulation, into x; then sp_region_fwd), eager
+    rs = None
+    if K:
+        xs = torch.empty(w.elems, dtype=x0.dtype, device=dev)
+
+        def unfused(s, with_fwd=True):
+            torch.sum(s["parts"].view(K, -1), dim=0, out=xs)
+            if with_fwd:
+                spr.sp_region_fwd(d, xs, bias, s["res"], gamma, beta, s["h"], s["y"], s["mask"],
+                                  s["mean"], s["rstd"], stream)
+
+        def eager_us(fn):
+            for i in range(3):
+                fn(sets[i % nsets])
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for i in range(args.steps):
+                fn(sets[i % nsets])
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / args.steps * 1e3
+
+        rs = {"nparts": K, "fused_fwd_us": round(float(kernel_us[0]), 2),
+              "unfused_sum_plus_fwd_us": round(eager_us(unfused), 2),
+              "unfused_sum_us": round(eager_us(lambda s: unfused(s, False)), 2),
+              "fused_fwd_eager_us": round(eager_us(fwd), 2)}
 
     # ---- layers of two calls (pre-attention and pre-MLP): call B's residual
     # is call A's h, and call A's backward takes call B's dresidual as dh_out
@@ -364,7 +413,8 @@ def main():
     names = ["sp_region_fwd"] + (
         ["sp_region_bwd_rows_kernel", "sp_region_bwd_finalize_kernel"] if n_bwd == 2 else
         ["sp_region_bwd_rowsum_kernel", "sp_region_bwd_main_kernel", "sp_region_bwd_finalize_kernel"])
-    fwd_b, bwd_rows_b, bwd_grad_b = algorithmic_bytes(w, mask_stored=not args.no_mask)
+    fwd_b, bwd_rows_b, bwd_grad_b = algorithmic_bytes(w, mask_stored=not args.no_mask,
+                                                      x_parts=max(K, 1))
     # algorithmic bytes of each launch (the split path's row-sum pass only re-reads)
     alg = [fwd_b] + ([bwd_rows_b, bwd_grad_b] if n_bwd == 2 else [0, bwd_rows_b, bwd_grad_b])
 
@@ -410,6 +460,9 @@ def main():
     }
     if layer is not None:
         out["layer"] = layer
+    if rs is not None:
+        out["rs_prologue"] = rs
+        out["config"]["rs_parts"] = K
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w)

@@ -70,6 +70,8 @@ def lib():
         P, D = ctypes.c_void_p, ctypes.POINTER(spr_desc)
         L.sp_region_fwd.argtypes = [D] + [P] * 10 + [P]
         L.sp_region_fwd.restype = ctypes.c_int
+        L.sp_region_fwd_rs.argtypes = [D, P, ctypes.c_int32] + [P] * 9 + [P]
+        L.sp_region_fwd_rs.restype = ctypes.c_int
         L.sp_region_bwd.argtypes = [D] + [P] * 12 + [P, ctypes.c_size_t, P]
         L.sp_region_bwd.restype = ctypes.c_int
         L.sp_region_bwd_num_launches.argtypes = [D]
@@ -151,6 +153,25 @@ def sp_region_fwd(d, x, bias, residual, gamma, beta, h_out, y_out, mask_out, mea
         raise SprError("sp_region_fwd", st)
 
 
+def sp_region_fwd_rs(d, x_parts, nparts, bias, residual, gamma, beta, h_out, y_out, mask_out,
+                     mean_out, rstd_out, stream=None):
+    """sp_region_fwd with x = the sum of nparts partial slabs x_parts
+    ([nparts, N, h], contiguous), added in the kernel's prologue."""
+    import torch
+    L = lib()
+    N, H, io, dev = d.rows, d.h, _io_dtype(d), x_parts.device if x_parts is not None else None
+    f32, u8 = torch.float32, torch.uint8
+    args = [_arg(x_parts, "x_parts", int(nparts) * N * H, io, dev), ctypes.c_int32(int(nparts)),
+            _arg(bias, "bias", H, f32, dev, True),
+            _arg(residual, "residual", N * H, io, dev), _arg(gamma, "gamma", H, f32, dev),
+            _arg(beta, "beta", H, f32, dev, True), _arg(h_out, "h_out", N * H, io, dev),
+            _arg(y_out, "y_out", N * H, io, dev), _arg(mask_out, "mask_out", N * H, u8, dev, True),
+            _arg(mean_out, "mean_out", N, f32, dev, True), _arg(rstd_out, "rstd_out", N, f32, dev)]
+    st = L.sp_region_fwd_rs(ctypes.byref(d.c()), *args, _stream(stream))
+    if st != SPR_OK:
+        raise SprError("sp_region_fwd_rs", st)
+
+
 def _bwd_args(d, dy, dh_out, h, mask, mean, rstd, gamma, dx_out, dres_out, dgamma_out,
               dbeta_out, dbias_out, workspace):
     import torch
@@ -222,6 +243,14 @@ def fwd(d, x, bias, residual, gamma, beta, stream=None, store_mask=True):
     o = alloc_fwd_outputs(d, x.device, store_mask)
     sp_region_fwd(d, x, bias, residual, gamma, beta, o["h"], o["y"], o["mask"], o["mean"],
                   o["rstd"], stream)
+    return o
+
+
+def fwd_rs(d, x_parts, nparts, bias, residual, gamma, beta, stream=None, store_mask=True):
+    """Allocates the outputs and runs sp_region_fwd_rs; returns them as a dict."""
+    o = alloc_fwd_outputs(d, x_parts.device, store_mask)
+    sp_region_fwd_rs(d, x_parts, nparts, bias, residual, gamma, beta, o["h"], o["y"], o["mask"],
+                     o["mean"], o["rstd"], stream)
     return o
 
 

@@ -170,6 +170,57 @@ __device__ __forceinline__ void load_x_res(const FwdArgs& a, int64_t row, const 
     }
 }
 
+// The reduce-scatter prologue: x = round_io(x_parts[0] + x_parts[1] + ...)
+// over the row's vectors, fp32 adds in rank order, then one rounding to the
+// I/O type.  Parts are loaded in groups of G, 8 vectors per thread in flight
+// (a group slot past the last part re-reads part 0 and does not add it), so
+// the prologue needs no more registers than the rest of the kernel.
+template <typename IO, int VPT>
+__device__ __forceinline__ void load_x_sum(const FwdArgs& a, int64_t row, const int (&vc)[VPT],
+                                           uint4 (&xq)[VPT]) {
+    using V = Vec<IO>;
+    constexpr int E = V::N;
+    const IO* base = static_cast<const IO*>(a.x) + row * a.hidden;
+    float acc[VPT][E];
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+        V v;
+        v.set(load_stream(base + (int64_t)vc[k] * E));
+#pragma unroll
+        for (int j = 0; j < E; ++j) acc[k][j] = v.v[j];
+    }
+    constexpr int G = VPT >= 8 ? 1 : 8 / VPT;
+    for (int p0 = 1; p0 < a.nparts; p0 += G) {
+        uint4 q[G][VPT];
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            const int p = p0 + i < a.nparts ? p0 + i : 0;
+#pragma unroll
+            for (int k = 0; k < VPT; ++k)
+                q[i][k] = load_stream(base + (int64_t)p * a.part_stride + (int64_t)vc[k] * E);
+        }
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            if (p0 + i < a.nparts) {
+#pragma unroll
+                for (int k = 0; k < VPT; ++k) {
+                    V v;
+                    v.set(q[i][k]);
+#pragma unroll
+                    for (int j = 0; j < E; ++j) acc[k][j] += v.v[j];
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+        V v;
+#pragma unroll
+        for (int j = 0; j < E; ++j) v.v[j] = acc[k][j];
+        xq[k] = v.get();
+    }
+}
+
 template <int VPT, int E>
 __device__ __forceinline__ void load_bias(const FwdArgs& a, const int (&vc)[VPT],
                                           float (&bb)[VPT][E]) {
@@ -196,7 +247,9 @@ __device__ __forceinline__ void load_affine(const FwdArgs& a, const int (&vc)[VP
 
 // Row kernel: one team per row.  WAVE_ROWS: each wave owns one row (short
 // rows, 4 rows per workgroup, no LDS); otherwise the whole workgroup owns
-// one row.  EXACT: the row is exactly VPT vectors per thread.
+// one row.  EXACT: the row is exactly VPT vectors per thread.  With
+// nparts > 1 it also runs the reduce-scatter prologue (x is the sum of
+// nparts partial slabs).
 //
 // Every load is issued unconditionally, so a thread has all its x and
 // residual vectors in flight at once; the dropout words, which need no
@@ -227,7 +280,14 @@ __global__ void __launch_bounds__(LB) sp_region_fwd_kernel(FwdArgs a) {
     bool ok[VPT];
     row_slots<VPT>(tid, tpr, a.nvec, EXACT, vc, ok);
     uint4 xq[VPT], rq[VPT];
-    load_x_res<IO, VPT>(a, row, vc, xq, rq);
+    if (a.nparts > 1) {                  // uniform: the reduce-scatter prologue
+        const IO* rr = static_cast<const IO*>(a.residual) + row * a.hidden;
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) rq[k] = load_stream(rr + (int64_t)vc[k] * E);
+        load_x_sum<IO, VPT>(a, row, vc, xq);
+    } else {
+        load_x_res<IO, VPT>(a, row, vc, xq, rq);
+    }
     float bb[VPT][E];
     load_bias<VPT, E>(a, vc, bb);
 
@@ -435,6 +495,7 @@ hipError_t launch_fwd(const spr_desc& d, const RowPlan& p, const FwdArgs& a, hip
         stream = a.rows > 4 * (int64_t)cus;
     }
     if (force && strcmp(force, "rows") == 0) stream = false;
+    if (a.nparts > 1) stream = false;    // the prologue is in the row kernel only
     if (stream)
         return d.io == SPR_BF16 ? fwd_stream_by_norm<__bf16>(d, sp, a, s)
                                 : fwd_stream_by_norm<float>(d, sp, a, s);

@@ -79,6 +79,8 @@ struct FwdArgs {
     float inv_h;           // 1 / h
     float eps;
     int nvec;
+    int nparts;            // > 1: x holds nparts partial slabs, summed in the kernel
+    int64_t part_stride;   // elements between two slabs (N * h)
 };
 
 struct BwdArgs {

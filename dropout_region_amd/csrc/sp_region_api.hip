@@ -206,6 +206,58 @@ spr_status check_desc(const spr_desc* d, RowPlan* plan, PlanKind kind) {
 
 }  // namespace
 
+namespace {
+
+constexpr int32_t kMaxParts = 1024;
+
+// Every check of the forward, then the launch.  x holds nparts slabs of
+// [N, h] (nparts == 1: the plain forward).
+spr_status fwd_impl(const spr_desc* d, const void* x, int nparts, const float* bias,
+                    const void* residual, const float* gamma, const float* beta, void* h_out,
+                    void* y_out, uint8_t* mask_out, float* mean_out, float* rstd_out,
+                    hipStream_t stream) {
+    RowPlan plan;
+    spr_status st = check_desc(d, &plan, kPlanForward);
+    if (st != SPR_OK) return st;
+    const bool ln = d->norm == SPR_LAYERNORM, drop = d->p > 0.0f;
+    if (!x || !residual || !gamma || !h_out || !y_out || !rstd_out) return SPR_ERR_INVALID_ARG;
+    if (ln != (beta != nullptr) || ln != (mean_out != nullptr)) return SPR_ERR_INVALID_ARG;
+    if (!drop) mask_out = nullptr;                                   // ignored at p == 0
+    const void* io16[] = {x, residual, h_out, y_out};
+    for (const void* p : io16)
+        if (!aligned(p, 16)) return SPR_ERR_INVALID_ARG;
+    if (!aligned(bias, 16) || !aligned(gamma, 16) || !aligned(beta, 16)) return SPR_ERR_INVALID_ARG;
+    if (!aligned(mask_out, 8) || !aligned(mean_out, 4) || !aligned(rstd_out, 4))
+        return SPR_ERR_INVALID_ARG;
+
+    const int64_t rows = d->s_local * d->b;
+    const uint64_t E = (uint64_t)rows * (uint64_t)d->h;
+    const uint64_t es = (d->io == SPR_BF16) ? 2u : 4u;
+    const uint64_t pb = (uint64_t)d->h * 4u, sb = (uint64_t)rows * 4u;
+    const Range outs[] = {range_of(h_out, E * es), range_of(y_out, E * es), range_of(mask_out, E),
+                          range_of(mean_out, sb), range_of(rstd_out, sb)};
+    const Range ins[] = {range_of(x, (uint64_t)nparts * E * es), range_of(residual, E * es),
+                         range_of(bias, pb),
+                         range_of(gamma, pb), range_of(beta, pb)};
+    if (!disjoint(outs, 5, ins, 5)) return SPR_ERR_INVALID_ARG;
+
+    FwdArgs a{};
+    a.x = x; a.bias = bias; a.residual = residual; a.gamma = gamma; a.beta = beta;
+    a.h_out = h_out; a.y_out = y_out; a.mask_out = mask_out; a.mean_out = mean_out;
+    a.rstd_out = rstd_out;
+    a.rows = rows;
+    a.hidden = d->h;
+    set_dropout(*d, rows, &a);
+    a.inv_h = (float)(1.0 / (double)d->h);
+    a.eps = d->eps;
+    a.nvec = plan.nvec;
+    a.nparts = nparts;
+    a.part_stride = (int64_t)E;
+    return launch_fwd(*d, plan, a, stream) == hipSuccess ? SPR_OK : SPR_ERR_HIP;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* sp_region_status_string(spr_status s) {
@@ -246,41 +298,17 @@ spr_status sp_region_fwd(const spr_desc* d, const void* x, const float* bias,
                          const void* residual, const float* gamma, const float* beta,
                          void* h_out, void* y_out, uint8_t* mask_out, float* mean_out,
                          float* rstd_out, hipStream_t stream) {
-    RowPlan plan;
-    spr_status st = check_desc(d, &plan, kPlanForward);
-    if (st != SPR_OK) return st;
-    const bool ln = d->norm == SPR_LAYERNORM, drop = d->p > 0.0f;
-    if (!x || !residual || !gamma || !h_out || !y_out || !rstd_out) return SPR_ERR_INVALID_ARG;
-    if (ln != (beta != nullptr) || ln != (mean_out != nullptr)) return SPR_ERR_INVALID_ARG;
-    if (!drop) mask_out = nullptr;                                   // ignored at p == 0
-    const void* io16[] = {x, residual, h_out, y_out};
-    for (const void* p : io16)
-        if (!aligned(p, 16)) return SPR_ERR_INVALID_ARG;
-    if (!aligned(bias, 16) || !aligned(gamma, 16) || !aligned(beta, 16)) return SPR_ERR_INVALID_ARG;
-    if (!aligned(mask_out, 8) || !aligned(mean_out, 4) || !aligned(rstd_out, 4))
-        return SPR_ERR_INVALID_ARG;
+    return fwd_impl(d, x, 1, bias, residual, gamma, beta, h_out, y_out, mask_out, mean_out,
+                    rstd_out, stream);
+}
 
-    const int64_t rows = d->s_local * d->b;
-    const uint64_t E = (uint64_t)rows * (uint64_t)d->h;
-    const uint64_t es = (d->io == SPR_BF16) ? 2u : 4u;
-    const uint64_t pb = (uint64_t)d->h * 4u, sb = (uint64_t)rows * 4u;
-    const Range outs[] = {range_of(h_out, E * es), range_of(y_out, E * es), range_of(mask_out, E),
-                          range_of(mean_out, sb), range_of(rstd_out, sb)};
-    const Range ins[] = {range_of(x, E * es), range_of(residual, E * es), range_of(bias, pb),
-                         range_of(gamma, pb), range_of(beta, pb)};
-    if (!disjoint(outs, 5, ins, 5)) return SPR_ERR_INVALID_ARG;
-
-    FwdArgs a{};
-    a.x = x; a.bias = bias; a.residual = residual; a.gamma = gamma; a.beta = beta;
-    a.h_out = h_out; a.y_out = y_out; a.mask_out = mask_out; a.mean_out = mean_out;
-    a.rstd_out = rstd_out;
-    a.rows = rows;
-    a.hidden = d->h;
-    set_dropout(*d, rows, &a);
-    a.inv_h = (float)(1.0 / (double)d->h);
-    a.eps = d->eps;
-    a.nvec = plan.nvec;
-    return launch_fwd(*d, plan, a, stream) == hipSuccess ? SPR_OK : SPR_ERR_HIP;
+spr_status sp_region_fwd_rs(const spr_desc* d, const void* x_parts, int32_t nparts,
+                            const float* bias, const void* residual, const float* gamma,
+                            const float* beta, void* h_out, void* y_out, uint8_t* mask_out,
+                            float* mean_out, float* rstd_out, hipStream_t stream) {
+    if (nparts < 1 || nparts > kMaxParts) return SPR_ERR_INVALID_ARG;
+    return fwd_impl(d, x_parts, nparts, bias, residual, gamma, beta, h_out, y_out, mask_out,
+                    mean_out, rstd_out, stream);
 }
 
 }  // extern "C"

@@ -132,6 +132,31 @@ spr_status sp_region_fwd(const spr_desc* desc,
                          float* mean_out, float* rstd_out,
                          hipStream_t stream);
 
+/* The forward with the reduce-scatter's arithmetic fused into its prologue.
+ * Under sequence parallelism the row-parallel linear's partial outputs are
+ * reduce-scattered instead of all-reduced, so rank i receives, for its own
+ * tokens, the sum over the t ranks' partial outputs ("Tensor and sequence
+ * parallelism -- explained with pictures", section "Add Sequence
+ * parallelism"; "SP: Partition Activations Alongside TP", section "Connect
+ * SP and TP across a layer").  This entry point takes those partial slabs
+ * and sums them itself, so the reduced x is never written to or read from
+ * memory:
+ *  x_parts  [nparts][N][h] io   the partial slabs of this shard's rows, one
+ *                               per rank in rank order (contiguous; slab p
+ *                               at element offset p*N*h)
+ *  nparts   1 .. 1024           (t for a direct reduce-scatter; 2 for the
+ *                               last step of a ring)
+ * x = round_io(x_parts[0] + x_parts[1] + ...): fp32 adds in rank order, one
+ * rounding to the I/O type -- bit-identical to summing the slabs that way
+ * and calling sp_region_fwd on the result.  Every other argument, check and
+ * output is sp_region_fwd's; nparts = 1 is sp_region_fwd. */
+spr_status sp_region_fwd_rs(const spr_desc* desc, const void* x_parts, int32_t nparts,
+                            const float* bias, const void* residual,
+                            const float* gamma, const float* beta,
+                            void* h_out, void* y_out, uint8_t* mask_out,
+                            float* mean_out, float* rstd_out,
+                            hipStream_t stream);
+
 /* Bytes of device workspace sp_region_bwd needs for this desc (fp32
  * column partials of dgamma/dbeta/dbias and the kernels' coordination
  * words).  0 on an invalid desc. */

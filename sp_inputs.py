@@ -14,6 +14,10 @@ Recipe (the pages measure on no dataset; activations are synthetic by nature):
   float32 -> bfloat16 conversion, and travel as raw uint16 bit patterns.
   Shard i of t is rows [i*s/t*b, (i+1)*s/t*b) of the full tensor (the
   sequence-major layout makes a shard one contiguous slab).
+  The partial slabs of the reduce-scatter prologue (make_parts): a second
+  generator, default_rng(seed + 1), draws nparts slabs of standard normals
+  in rank order, each scaled by 1/sqrt(nparts) so that their sum has the
+  unit variance of x.
 """
 from dataclasses import dataclass, field
 
@@ -48,6 +52,15 @@ def make_inputs(rows, h, io, seed=0, dh_out=False):
     return {"x": cast(x), "residual": cast(residual), "dy": cast(dy),
             "dh_out": None if dho is None else cast(dho),
             "bias": bias, "beta": beta, "gamma": gamma}
+
+
+def make_parts(rows, h, io, nparts, seed=0):
+    """nparts partial slabs [nparts, rows*h] of the row-parallel output, in
+    the I/O type (see the module recipe)."""
+    rng = np.random.default_rng(seed + 1)
+    scale = np.float32(1.0 / np.sqrt(nparts))
+    parts = rng.standard_normal((nparts, rows * h), dtype=np.float32) * scale
+    return to_bf16_bits(parts) if io == BF16 else parts
 
 
 @dataclass

@@ -173,6 +173,17 @@ def gpu_fwd(d, inp, with_bias=True, device="cuda:0", path=None, store_mask=True)
     return {k: to_host(v) for k, v in o.items()}
 
 
+def gpu_fwd_rs(d, inp, parts, nparts, with_bias=True, device="cuda:0"):
+    """sp_region_fwd_rs on the GPU: x is the sum of the nparts slabs `parts`."""
+    import dropout_region_amd as spr
+    io = d.io
+    o = spr.fwd_rs(d, to_device(np.ascontiguousarray(parts).ravel(), io, device), nparts,
+                   to_device(inp["bias"], device=device) if with_bias else None,
+                   to_device(inp["residual"], io, device), to_device(inp["gamma"], device=device),
+                   to_device(inp["beta"], device=device) if d.norm == 0 else None)
+    return {k: to_host(v) for k, v in o.items()}
+
+
 def gpu_bwd(d, inp, saved, with_dh_out=False, want_dbias=True, device="cuda:0", repeat=1,
             path=None):
     """Backward from `saved` (host arrays of h, mask, mean, rstd).  With

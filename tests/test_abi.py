@@ -29,7 +29,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    assert names == sorted(["sp_region_fwd", "sp_region_bwd", "sp_region_bwd_workspace_bytes",
+    assert names == sorted(["sp_region_fwd", "sp_region_fwd_rs", "sp_region_bwd",
+                            "sp_region_bwd_workspace_bytes",
                             "sp_region_bwd_num_launches", "sp_region_bwd_launch",
                             "sp_region_activation_bytes", "sp_region_status_string"])
 
@@ -75,6 +76,22 @@ FWD_OK = [A, A + 0x100000, A + 0x200000, A + 0x300000, A + 0x310000, A + 0x40000
 def test_fwd_rejects_bad_desc(L, field, value, status):
     d = _good_desc(**{field: value})
     assert _fwd_raw(L, d, FWD_OK) == status
+
+
+def _fwd_rs_raw(L, d, nparts, ptrs):
+    return L.sp_region_fwd_rs(ctypes.byref(d), ctypes.c_void_p(ptrs[0]), ctypes.c_int32(nparts),
+                              *[ctypes.c_void_p(p) for p in ptrs[1:]], None)
+
+
+def test_fwd_rs_checks(L):
+    d = _good_desc()                             # N*h*2 = 1 KiB per slab
+    assert _fwd_rs_raw(L, d, 0, FWD_OK) == spr.SPR_ERR_INVALID_ARG
+    assert _fwd_rs_raw(L, d, -3, FWD_OK) == spr.SPR_ERR_INVALID_ARG
+    assert _fwd_rs_raw(L, d, 1025, FWD_OK) == spr.SPR_ERR_INVALID_ARG
+    bad = list(FWD_OK)
+    bad[5] = FWD_OK[0] + 3 * 1024                # h_out inside slab 3 of 4
+    assert _fwd_rs_raw(L, d, 4, bad) == spr.SPR_ERR_INVALID_ARG
+    assert _fwd_rs_raw(L, _good_desc(h=60), 4, FWD_OK) == spr.SPR_ERR_UNSUPPORTED
 
 
 def test_fwd_pointer_rules(L):

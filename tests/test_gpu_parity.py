@@ -13,7 +13,7 @@ import pytest
 
 import dropout_region_amd as spr
 import oracle
-from sp_inputs import WORKLOADS, make_inputs
+from sp_inputs import WORKLOADS, make_inputs, make_parts
 from tests import parity as P
 
 pytestmark = pytest.mark.gpu
@@ -130,6 +130,40 @@ def test_mask_free_region(name):
     for k in ("dx", "dres", "dgamma", "dbeta", "dbias"):
         if stored.get(k) is not None:
             P.exact(f"{k} (regenerated vs stored mask)", regen[k], stored[k])
+
+
+# The reduce-scatter prologue: x is the sum of nparts partial slabs, added
+# in the forward kernel.
+RS = {
+    "bf16_ln_h6144_t8": (base(s_local=16, b=4, h=6144, shard_index=3, t=8), 8),
+    "bf16_ln_h6144_ring_last_step": (base(s_local=16, b=4, h=6144, shard_index=3, t=8), 2),
+    "bf16_ln_h6144_one_part": (base(s_local=16, b=4, h=6144, shard_index=3, t=8), 1),
+    "bf16_rms_h8192_5_parts": (base(s_local=20, b=1, h=8192, norm=RMS, eps=1e-6), 5),
+    "fp32_ln_h260_ragged_3_parts": (base(s_local=13, b=3, h=260, io=F32), 3),
+    "bf16_ln_h25600_t2": (base(s_local=3, b=2, h=25600, shard_index=1, t=2), 2),
+    "bf16_ln_h32768_widest_9_parts": (base(s_local=2, b=1, h=32768), 9),
+    "bf16_ln_h8192_1100_rows_t4": (base(s_local=1100, b=1, h=8192, t=4, shard_index=2), 4),
+    "bf16_ln_h1000_wave_rows_p0_6_parts": (base(s_local=37, b=1, h=1000, p=0.0), 6),
+}
+
+
+@pytest.mark.parametrize("name", sorted(RS))
+def test_reduce_scatter_prologue(name):
+    kw, nparts = RS[name]
+    d, od = descs(**kw)
+    seed = zlib.crc32(name.encode()) % 1000
+    _say(f"[case] reduce-scatter prologue {name}: {kw} nparts={nparts}")
+    inp = make_inputs(d.rows, d.h, d.io, seed=seed)
+    parts = make_parts(d.rows, d.h, d.io, nparts, seed=seed)
+    x = oracle.reduce_parts(od, parts)
+    want = P.oracle_fwd(od, dict(inp, x=x))
+    got = P.gpu_fwd_rs(d, inp, parts, nparts)
+    P.check_fwd(got, want, d.io)
+    # bit-identical to the plain forward (same kernel) on the summed x
+    plain = P.gpu_fwd(d, dict(inp, x=x), path="rows")
+    for k in ("h", "y", "mask", "mean", "rstd"):
+        if plain[k] is not None:
+            P.exact(f"{k} (fused prologue vs summed x)", got[k], plain[k])
 
 
 @pytest.mark.parametrize("with_bias,with_dh_out,want_dbias", [(False, False, True),
