@@ -20,6 +20,8 @@
 #include "sp_device.h"
 #include "sp_plan.h"
 
+
+
 namespace spr {
 
 // The saved tensors of one row as loaded (raw words; decoded when used).
@@ -32,9 +34,8 @@ struct RowIn {
 
 template <typename IO, int NORM, int DROP, int VPT, bool WAVE_ROWS, int LB>
 __global__ void __launch_bounds__(LB) sp_region_bwd_rows_kernel(BwdArgs a) {
-    // Prefetching the next row doubles the row's registers; wide rows
-    // (more than two vectors per thread) load each row when they reach it.
-    constexpr bool PREFETCH = VPT <= 2;
+    // Rows in flight per thread (each costs the row's registers again).
+    constexpr int DEPTH = bwd_depth(VPT, LB, WAVE_ROWS, NORM == SPR_LAYERNORM);
     using V = Vec<IO>;
     constexpr int E = V::N;
     constexpr int MW = E / 4;                 // mask words per vector
@@ -92,24 +93,10 @@ __global__ void __launch_bounds__(LB) sp_region_bwd_rows_kernel(BwdArgs a) {
         in.rs = a.rstd[row];
     };
 
-    // Rows team, team + teams, ...: the trip count is uniform over the team
-    // (the workgroup, when the workgroup is the team), so every thread meets
-    // every barrier.  The next row's loads are issued before this row's
-    // reduction, so they are in flight while it is computed and stored.
-    RowIn<VPT, MW> cur, nxt;
-    int64_t row = team;
-    if (PREFETCH && row < a.rows) load_row(row, cur);
-    int slot = 0;
-    for (; row < a.rows; row += a.teams) {
-        const int64_t next = row + a.teams;
-        if (PREFETCH) {
-            if (next < a.rows) load_row(next, nxt);
-        } else {
-            load_row(row, cur);
-        }
-
-        // Regenerated dropout: the row's keep bits, drawn while the row's
-        // loads are in flight.
+    // One row: the two row sums (one team reduction through `slot`), then
+    // dx/dresidual and the column partials.
+    auto process = [&](int64_t row, const RowIn<VPT, MW>& cur, float* slot) {
+        // Regenerated dropout: the row's keep bits.
         uint32_t kbits[VPT];
         if (DROP == kDropRegen) {
 #pragma unroll
@@ -135,8 +122,7 @@ __global__ void __launch_bounds__(LB) sp_region_bwd_rows_kernel(BwdArgs a) {
                 }
             }
         }
-        block_sum2(s1, s2, red[slot], nwaves);
-        slot ^= 1;
+        block_sum2(s1, s2, slot, nwaves);
         const float mg = s1 * a.inv_h, mgx = s2 * a.inv_h;
 
         const int64_t rbase = row * a.hidden;
@@ -174,7 +160,44 @@ __global__ void __launch_bounds__(LB) sp_region_bwd_rows_kernel(BwdArgs a) {
                 dx.store(static_cast<IO*>(a.dx_out) + off);
             }
         }
-        if (PREFETCH) cur = nxt;
+    };
+
+    // Rows team, team + teams, ...: the trip count is uniform over the team
+    // (the workgroup, when the workgroup is the team), so every thread meets
+    // every barrier.  Consecutive rows alternate the two reduction slots.
+    // Narrow rows keep DEPTH rows in flight: a ring of DEPTH row buffers,
+    // each refilled with the row DEPTH steps ahead as soon as its row is
+    // done, so DEPTH - 1 rows are loading while one is computed.
+    int slot = 0;
+    if constexpr (DEPTH > 1) {
+        RowIn<VPT, MW> buf[DEPTH];
+#pragma unroll
+        for (int i = 0; i < DEPTH; ++i) {
+            const int64_t r = team + i * a.teams;
+            if (r < a.rows) load_row(r, buf[i]);
+        }
+        int64_t row = team;
+        bool more = row < a.rows;
+        while (more) {
+#pragma unroll
+            for (int i = 0; i < DEPTH; ++i) {
+                if (more) {
+                    process(row, buf[i], red[slot]);
+                    slot ^= 1;
+                    const int64_t ahead = row + DEPTH * a.teams;
+                    if (ahead < a.rows) load_row(ahead, buf[i]);
+                    row += a.teams;
+                    more = row < a.rows;
+                }
+            }
+        }
+    } else {
+        RowIn<VPT, MW> cur;
+        for (int64_t row = team; row < a.rows; row += a.teams) {
+            load_row(row, cur);
+            process(row, cur, red[slot]);
+            slot ^= 1;
+        }
     }
 
     float* part = a.partials + team * 3 * a.hidden;
@@ -472,7 +495,16 @@ static hipError_t bwd_by_vpt(const RowPlan& p, const BwdArgs& a, hipStream_t s) 
     } else {
         // must match kBwdCombos
         switch (p.vpt) {
-            SPR_BWD_CASE(1, 1024) SPR_BWD_CASE(2, 768) SPR_BWD_CASE(3, 512)
+            case 1:
+                if (p.lb == 768) {
+                    hipLaunchKernelGGL((sp_region_bwd_rows_kernel<IO, NORM, DROP, 1, WR, 768>), g, b,
+                                       0, s, a);
+                } else {
+                    hipLaunchKernelGGL((sp_region_bwd_rows_kernel<IO, NORM, DROP, 1, WR, 1024>), g,
+                                       b, 0, s, a);
+                }
+                break;
+            SPR_BWD_CASE(2, 768) SPR_BWD_CASE(3, 512)
             SPR_BWD_CASE(4, 512) SPR_BWD_CASE(5, 640) SPR_BWD_CASE(6, 512) SPR_BWD_CASE(8, 512)
             default: return hipErrorInvalidValue;
         }

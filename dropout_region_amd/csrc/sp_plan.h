@@ -31,10 +31,23 @@ struct VptBound {
 };
 static constexpr VptBound kWgCombos[] = {{1, 1024}, {2, 1024}, {3, 1024}, {4, 1024},
                                          {5, 768},  {6, 768},  {8, 512}};
-// The backward runs one workgroup per CU, keeps three column accumulators
-// per element in registers, so its bound tracks the workgroup it needs.
-static constexpr VptBound kBwdCombos[] = {{1, 1024}, {2, 768}, {3, 512}, {4, 512},
-                                          {5, 640},  {6, 512}, {8, 512}};
+// The backward runs one workgroup per CU and keeps three column accumulators
+// per element and DEPTH rows in flight in registers, so its bound tracks the
+// workgroup it needs.  One vector per thread has two bounds: 768 threads
+// leave room for three rows in flight, 1024 threads (rows of up to 1024
+// vectors) for two.  A plan takes the smallest bound that fits its team.
+static constexpr VptBound kBwdCombos[] = {{1, 768}, {1, 1024}, {2, 768}, {3, 512},
+                                          {4, 512}, {5, 640},  {6, 512}, {8, 512}};
+
+// Rows in flight per thread in the backward's row kernel (measured on
+// MI355X): one vector per thread -> three rows (two at 1024 threads with
+// LayerNorm, where a third would spill), two vectors -> none ahead (a
+// prefetch row spills at 768 threads and was slower even at one ahead),
+// wider rows -> none.  Short one-wave rows keep one row ahead.
+constexpr int bwd_depth(int vpt, int lb, bool wave_rows, bool layernorm) {
+    return wave_rows ? (vpt <= 2 ? 2 : 1)
+                     : (vpt == 1 ? ((lb <= 768 || !layernorm) ? 3 : 2) : 1);
+}
 
 enum PlanKind { kPlanForward, kPlanBackward };
 

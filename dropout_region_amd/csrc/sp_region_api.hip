@@ -36,11 +36,14 @@ bool make_row_plan(int io, int64_t h, PlanKind kind, RowPlan* plan) {
     int64_t best_tpr = 0, best_waste = INT64_MAX;
     for (int i = 0; i < 7; ++i) {
         const int v = order[i];
-        int lb = 0;
-        for (const VptBound& c : (kind == kPlanForward) ? kWgCombos : kBwdCombos)
-            if (c.vpt == v) lb = c.lb;
         const int64_t tpr = ((nvec + v - 1) / v + 63) / 64 * 64;
-        if (tpr > lb) continue;
+        const VptBound* tab = (kind == kPlanForward) ? kWgCombos : kBwdCombos;
+        const int ntab = (kind == kPlanForward) ? (int)(sizeof kWgCombos / sizeof kWgCombos[0])
+                                                : (int)(sizeof kBwdCombos / sizeof kBwdCombos[0]);
+        int lb = 0;                          // the smallest compiled bound that fits
+        for (int t = 0; t < ntab; ++t)
+            if (tab[t].vpt == v && tab[t].lb >= tpr && (lb == 0 || tab[t].lb < lb)) lb = tab[t].lb;
+        if (lb == 0) continue;
         const int64_t waste = tpr * v - nvec;
         if (waste < best_waste) {
             best_waste = waste;
