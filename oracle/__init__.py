@@ -166,9 +166,12 @@ def reduce_parts(d, parts, L=None):
     return x
 
 
-def fwd(d, x, bias, residual, gamma, beta, rows=None, L=None):
+def fwd(d, x, bias, residual, gamma, beta, rows=None, L=None, write_h=True):
     """Forward over rows [r0, r1) (default: the whole shard).  x and residual
-    hold exactly those rows.  Returns dict h, y, mask, mean, rstd."""
+    hold exactly those rows.  Returns dict h, y, mask, mean, rstd.
+    x = None: the norm-only entry (h is the residual; write_h=False leaves
+    h unwritten, returned as None); gamma = None: the norm-free exit (h and
+    mask only)."""
     L = L or lib()
     r0, r1 = rows if rows is not None else (0, d.rows)
     n, H, io = r1 - r0, d.h, _io_dtype(d)
@@ -177,10 +180,12 @@ def fwd(d, x, bias, residual, gamma, beta, rows=None, L=None):
     bias = _check(bias, np.float32, H, "bias")
     gamma = _check(gamma, np.float32, H, "gamma")
     beta = _check(beta, np.float32, H, "beta")
-    out = {"h": np.empty(n * H, io), "y": np.empty(n * H, io),
-           "mask": np.empty(n * H, np.uint8) if d.p > 0 else None,
-           "mean": np.empty(n, np.float32) if d.norm == LAYERNORM else None,
-           "rstd": np.empty(n, np.float32)}
+    norm = gamma is not None
+    out = {"h": np.empty(n * H, io) if (x is not None or write_h) else None,
+           "y": np.empty(n * H, io) if norm else None,
+           "mask": np.empty(n * H, np.uint8) if d.p > 0 and x is not None else None,
+           "mean": np.empty(n, np.float32) if norm and d.norm == LAYERNORM else None,
+           "rstd": np.empty(n, np.float32) if norm else None}
     rc = L.spo_fwd(ctypes.byref(d.c()), r0, r1, _ptr(x), _ptr(bias), _ptr(residual),
                    _ptr(gamma), _ptr(beta), _ptr(out["h"]), _ptr(out["y"]),
                    _ptr(out["mask"]), _ptr(out["mean"]), _ptr(out["rstd"]))
@@ -189,9 +194,11 @@ def fwd(d, x, bias, residual, gamma, beta, rows=None, L=None):
     return out
 
 
-def bwd(d, dy, dh_out, h, mask, mean, rstd, gamma, want_dbias=True, rows=None, L=None):
+def bwd(d, dy, dh_out, h, mask, mean, rstd, gamma, want_dbias=True, rows=None, L=None,
+        want_dx=True, want_dres=True):
     """Backward over rows [r0, r1).  Returns dict dx, dres, dgamma, dbeta,
-    dbias (parameter gradients are partial sums over those rows)."""
+    dbias (parameter gradients are partial sums over those rows).
+    dy = None: the norm-free exit (dh = dh_out; no dgamma/dbeta)."""
     L = L or lib()
     r0, r1 = rows if rows is not None else (0, d.rows)
     n, H, io = r1 - r0, d.h, _io_dtype(d)
@@ -202,9 +209,11 @@ def bwd(d, dy, dh_out, h, mask, mean, rstd, gamma, want_dbias=True, rows=None, L
     mean = _check(mean, np.float32, n, "mean")
     rstd = _check(rstd, np.float32, n, "rstd")
     gamma = _check(gamma, np.float32, H, "gamma")
-    out = {"dx": np.empty(n * H, io), "dres": np.empty(n * H, io),
-           "dgamma": np.empty(H, np.float32),
-           "dbeta": np.empty(H, np.float32) if d.norm == LAYERNORM else None,
+    norm = dy is not None
+    out = {"dx": np.empty(n * H, io) if want_dx else None,
+           "dres": np.empty(n * H, io) if want_dres else None,
+           "dgamma": np.empty(H, np.float32) if norm else None,
+           "dbeta": np.empty(H, np.float32) if norm and d.norm == LAYERNORM else None,
            "dbias": np.empty(H, np.float32) if want_dbias else None}
     rc = L.spo_bwd(ctypes.byref(d.c()), r0, r1, _ptr(dy), _ptr(dh_out), _ptr(h), _ptr(mask),
                    _ptr(mean), _ptr(rstd), _ptr(gamma), _ptr(out["dx"]), _ptr(out["dres"]),

@@ -269,8 +269,19 @@ int spo_fwd(const spo_desc* d, int64_t r0, int64_t r1,
     if (!desc_ok(d)) return -1;
     const int64_t N = rows_of(d), H = d->h;
     if (r0 < 0 || r1 < r0 || r1 > N) return -1;
-    if (!x || !residual || !gamma || !h_out || !y_out || !rstd_out) return -1;
-    if (!ptr_rules_fwd(d, beta, mean_out, mask_out)) return -1;
+    if (!residual || (!x && !gamma)) return -1;
+    if (x) {                                   /* the branch: x (+ bias), dropout */
+        if (!h_out || (d->p > 0.0f && !mask_out)) return -1;
+    } else {                                   /* norm-only entry: h is the residual */
+        if (bias || mask_out) return -1;
+    }
+    if (gamma) {                               /* the norm */
+        if (!y_out || !rstd_out) return -1;
+        if (d->norm == SPO_LAYERNORM && (!beta || !mean_out)) return -1;
+        if (d->norm == SPO_RMSNORM && (beta || mean_out)) return -1;
+    } else {                                   /* norm-free exit */
+        if (beta || y_out || mean_out || rstd_out) return -1;
+    }
 
     const float scale = spo_dropout_scale(d->p);
     double* hrow = (double*)malloc((size_t)H * sizeof(double));
@@ -279,6 +290,11 @@ int spo_fwd(const spo_desc* d, int64_t r0, int64_t r1,
     for (int64_t r = r0; r < r1; ++r) {
         for (int64_t c = 0; c < H; ++c) {
             int64_t i = (r - r0) * H + c;
+            if (!x) {                          /* no branch: h = residual, bit for bit */
+                float hf = load_io(d->io, residual, i);
+                hrow[c] = (double)(h_out ? store_io(d->io, h_out, i, hf) : hf);
+                continue;
+            }
             float u = load_io(d->io, x, i) + (bias ? bias[c] : 0.0f);   /* fp32 add */
             int keep = keep_elem(d, r, c);
             float v = keep ? u * scale : 0.0f;                          /* fp32 mul */
@@ -286,6 +302,7 @@ int spo_fwd(const spo_desc* d, int64_t r0, int64_t r1,
             hrow[c] = (double)store_io(d->io, h_out, i, hf);            /* norm reads rounded h */
             if (d->p > 0.0f) mask_out[i] = (uint8_t)keep;
         }
+        if (!gamma) continue;
         double mu, rs;
         row_stats(hrow, H, d->norm, (double)d->eps, &mu, &rs);
         for (int64_t c = 0; c < H; ++c) {
@@ -316,10 +333,14 @@ int spo_bwd(const spo_desc* d, int64_t r0, int64_t r1,
     if (!desc_ok(d)) return -1;
     const int64_t N = rows_of(d), H = d->h;
     if (r0 < 0 || r1 < r0 || r1 > N) return -1;
-    if (!dy || !h || !rstd || !gamma || !dx_out || !dres_out || !dgamma_out) return -1;
-    if (d->norm == SPO_LAYERNORM && (!mean || !dbeta_out)) return -1;
-    if (d->norm == SPO_RMSNORM && dbeta_out) return -1;
     if (d->p > 0.0f && !mask) return -1;
+    if (dy) {                                  /* through the norm */
+        if (!h || !rstd || !gamma || !dres_out || !dgamma_out) return -1;
+        if (d->norm == SPO_LAYERNORM && (!mean || !dbeta_out)) return -1;
+        if (d->norm == SPO_RMSNORM && dbeta_out) return -1;
+    } else {                                   /* norm-free exit: dh = dh_out */
+        if (!dh_out || !dx_out || dgamma_out || dbeta_out) return -1;
+    }
 
     const double scale = (double)spo_dropout_scale(d->p);
     double* buf = (double*)calloc((size_t)H * 8u, sizeof(double));
@@ -329,28 +350,33 @@ int spo_bwd(const spo_desc* d, int64_t r0, int64_t r1,
     double* acc_dgamma = buf + 5 * H;  double* acc_dbeta = buf + 6 * H;
     double* acc_dbias = buf + 7 * H;
 
-    for (int64_t c = 0; c < H; ++c) gam[c] = (double)gamma[c];
+    if (dy)
+        for (int64_t c = 0; c < H; ++c) gam[c] = (double)gamma[c];
     for (int64_t r = r0; r < r1; ++r) {
-        for (int64_t c = 0; c < H; ++c) {
-            hrow[c] = (double)load_io(d->io, h, (r - r0) * H + c);
-            dyrow[c] = (double)load_io(d->io, dy, (r - r0) * H + c);
+        if (dy) {
+            for (int64_t c = 0; c < H; ++c) {
+                hrow[c] = (double)load_io(d->io, h, (r - r0) * H + c);
+                dyrow[c] = (double)load_io(d->io, dy, (r - r0) * H + c);
+            }
+            double mu = (d->norm == SPO_LAYERNORM) ? (double)mean[r - r0] : 0.0;
+            norm_row_backward(H, d->norm, mu, (double)rstd[r - r0], hrow, dyrow, gam, xhat, dh);
         }
-        double mu = (d->norm == SPO_LAYERNORM) ? (double)mean[r - r0] : 0.0;
-        norm_row_backward(H, d->norm, mu, (double)rstd[r - r0], hrow, dyrow, gam, xhat, dh);
         for (int64_t c = 0; c < H; ++c) {
             int64_t i = (r - r0) * H + c;
-            double dhv = dh[c] + (dh_out ? (double)load_io(d->io, dh_out, i) : 0.0);
+            double dhv = (dy ? dh[c] : 0.0) + (dh_out ? (double)load_io(d->io, dh_out, i) : 0.0);
             int keep = (d->p > 0.0f) ? (mask[i] != 0) : 1;
             double dxu = keep ? dhv * scale : 0.0;
-            store_io(d->io, dres_out, i, (float)dhv);
-            store_io(d->io, dx_out, i, (float)dxu);
-            acc_dgamma[c] += dyrow[c] * xhat[c];
-            acc_dbeta[c] += dyrow[c];
+            if (dres_out) store_io(d->io, dres_out, i, (float)dhv);
+            if (dx_out) store_io(d->io, dx_out, i, (float)dxu);
+            if (dy) {
+                acc_dgamma[c] += dyrow[c] * xhat[c];
+                acc_dbeta[c] += dyrow[c];
+            }
             acc_dbias[c] += dxu;
         }
     }
     for (int64_t c = 0; c < H; ++c) {
-        dgamma_out[c] = (float)acc_dgamma[c];
+        if (dgamma_out) dgamma_out[c] = (float)acc_dgamma[c];
         if (dbeta_out) dbeta_out[c] = (float)acc_dbeta[c];
         if (dbias_out) dbias_out[c] = (float)acc_dbias[c];
     }

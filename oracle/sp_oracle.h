@@ -87,6 +87,13 @@ int spo_reduce_parts(const spo_desc* d, int nparts, const void* parts, void* x_o
  * lives at index (r - r0) * h + c, and r only enters the global index.
  * bias may be NULL (the same as a zero bias: u = x + 0.0f).  beta and
  * mean_out must be NULL for RMSNorm.  mask_out is not written when p == 0 (may be NULL).
+ * Two variants at the ends of the layer stack (a block boundary with no
+ * branch before the first LayerNorm, and none after the last residual add):
+ *  - x == NULL, the norm-only entry: no branch, h is the residual bit for
+ *    bit (no add), y = Norm(residual); bias and mask_out must be NULL, h_out
+ *    may be NULL (then h is not written);
+ *  - gamma == NULL, the norm-free exit: h and the mask only; beta, y_out,
+ *    mean_out and rstd_out must be NULL.
  * Returns 0 on success, -1 on an invalid argument.
  * Pinned: p=0 identity, dropout expectation, LayerNorm/RMSNorm closed forms,
  * float64 torch layer_norm / rms_norm, shard invariance. */
@@ -100,7 +107,10 @@ int spo_fwd(const spo_desc* d, int64_t r0, int64_t r1,
  * Uses the stored h, mask, mean and rstd of the forward.  dh_out (gradient reaching h from elsewhere, e.g. the next block's
  * residual branch) may be NULL.  dgamma/dbeta/dbias receive the partial sums
  * over rows [r0, r1) (fp32); dbeta must be NULL for RMSNorm; dbias may be
- * NULL.  mask may be NULL when p == 0.
+ * NULL.  mask may be NULL when p == 0.  dx_out may be NULL (not written:
+ * the norm-only entry has no branch).  dy == NULL is the norm-free exit:
+ * dh = dh_out (required), h, mean, rstd and gamma are not read,
+ * dgamma_out and dbeta_out must be NULL, dres_out may be NULL.
  * Pinned: central finite differences of spo_fwd_exact, float64 torch
  * autograd, the per-row identity sum_c dh = 0 for LayerNorm. */
 int spo_bwd(const spo_desc* d, int64_t r0, int64_t r1,

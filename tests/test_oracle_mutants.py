@@ -57,12 +57,17 @@ MUTANTS = {
     "dgamma_uses_g": ("acc_dgamma[c] += dyrow[c] * xhat[c];",
                       "acc_dgamma[c] += dyrow[c] * gam[c] * xhat[c];"),
     "dbias_ignores_mask": ("acc_dbias[c] += dxu;", "acc_dbias[c] += dhv;"),
-    "dx_not_scaled": ("double dxu = keep ? dhv * scale : 0.0;\n            store_io",
-                      "double dxu = keep ? dhv : 0.0;\n            store_io"),
-    "dh_out_ignored": ("double dhv = dh[c] + (dh_out ? (double)load_io(d->io, dh_out, i) : 0.0);",
-                       "double dhv = dh[c];"),
+    "dx_not_scaled": ("double dxu = keep ? dhv * scale : 0.0;\n            if (dres_out)",
+                      "double dxu = keep ? dhv : 0.0;\n            if (dres_out)"),
+    "dh_out_ignored": ("double dhv = (dy ? dh[c] : 0.0) + (dh_out ? (double)load_io(d->io, dh_out, i) : 0.0);",
+                       "double dhv = (dy ? dh[c] : 0.0);"),
     "exact_dgamma_uses_g": ("dgamma_out[c] += dy[i] * xhat[c];",
                             "dgamma_out[c] += dy[i] * gamma[c] * xhat[c];"),
+    # region variants
+    "entry_adds_zero": ("float hf = load_io(d->io, residual, i);\n                hrow[c]",
+                        "float hf = load_io(d->io, residual, i) + 0.0f;\n                hrow[c]"),
+    "exit_dres_scaled": ("if (dres_out) store_io(d->io, dres_out, i, (float)dhv);",
+                         "if (dres_out) store_io(d->io, dres_out, i, (float)(dy ? dhv : dxu));"),
     # reduce-scatter prologue
     "reduce_reversed_order": ("float acc = load_io(d->io, parts, i);                       /* rank 0 */\n"
                               "        for (int p = 1; p < nparts; ++p)",
@@ -82,7 +87,11 @@ def _checks(L, philox):
     """Pin checks, each a callable raising on failure (all run against L)."""
     from tests import test_oracle_accounting as A
     from tests import test_oracle_rs as S
+    from tests import test_oracle_variants as V
     c = [
+        lambda: V.test_entry_h_is_the_residual_bit_for_bit(L, F32),
+        lambda: V.test_entry_backward_matches_torch_autograd(L, LN),
+        lambda: V.test_exit_backward_matches_torch_autograd(L, 0.3),
         lambda: S.test_one_part_is_the_identity(L, BF16),
         lambda: S.test_integer_parts_sum_exactly(L, F32, 8),
         lambda: S.test_integer_parts_sum_exactly(L, BF16, 4),
