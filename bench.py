@@ -45,6 +45,27 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
+def variant_bytes(w, variant):
+    """Algorithmic bytes (fwd, bwd) of the two variants of the region.
+    entry: fwd reads residual, writes y (+ stats); bwd reads dy, h (the
+           residual) and the stats, writes dresidual, reads gamma, writes
+           dgamma/dbeta.
+    exit : fwd reads x, residual, writes h and the mask (+ bias); bwd reads
+           dh_out and the mask, writes dx and dbias."""
+    E, N, H = w.elems, w.rows, w.h
+    es = 2 if w.io == 1 else 4
+    ln = w.norm == 0
+    n_stat = 2 if ln else 1
+    if variant == "entry":
+        fwd = E * 2 * es + (2 if ln else 1) * H * 4 + n_stat * N * 4
+        bwd = E * 3 * es + n_stat * N * 4 + H * 4 + (2 if ln else 1) * H * 4
+    else:
+        m = 1 if w.p > 0 else 0
+        fwd = E * (3 * es + m) + H * 4
+        bwd = E * (2 * es + m) + H * 4
+    return fwd, bwd
+
+
 def algorithmic_bytes(w, with_bias=True, with_dh_out=False, mask_stored=True, x_parts=1):
     """Bytes the region must move per call (re-reads, partial sums and
     spills excluded).
@@ -196,6 +217,9 @@ def main():
     ap.add_argument("--rs-parts", type=int, default=0,
                     help="forward with the reduce-scatter prologue over this many partial "
                          "slabs (sp_region_fwd_rs); 0 = the plain forward")
+    ap.add_argument("--variant", choices=("full", "entry", "exit"), default="full",
+                    help="entry: the norm-only entry (no x, p = 0); exit: the norm-free exit "
+                         "(no norm; backward sp_region_bwd_exit)")
     ap.add_argument("--no-mask", action="store_true",
                     help="mask-free region: the forward stores no mask, the backward "
                          "regenerates the dropout decisions")
@@ -223,8 +247,11 @@ def main():
 
     w = WORKLOADS[wname]
     dev = torch.device("cuda:0")
+    V = args.variant
     d = spr.Desc(s_local=w.s_local, b=w.b, h=w.h, shard_index=0, t=w.t, io=w.io, norm=w.norm,
-                 p=w.p, eps=w.eps, seed=w.seed, offset=0)
+                 p=0.0 if V == "entry" else w.p, eps=w.eps, seed=w.seed, offset=0)
+    if V != "full" and (args.rs_parts or args.no_mask):
+        sys.exit("bench.py: --variant takes neither --rs-parts nor --no-mask")
     spr.lib()
     print(f"[bench] workload {w.name}: shard [{w.s_local}, {w.b}, {w.h}] N={w.rows} "
           f"on {torch.cuda.get_device_name(0)}", file=sys.stderr, flush=True)
@@ -241,21 +268,43 @@ def main():
         od = oracle.Desc(**{k: getattr(d, k) for k in ("s_local", "b", "h", "shard_index", "t",
                                                          "io", "norm", "p", "eps", "seed",
                                                          "offset")})
-        if K:
+        if V != "full":
+            ln = w.norm == 0
+            rr = slice(0, 2 * w.h)
+            odv = oracle.Desc(**{**od.__dict__, "s_local": 2, "b": 1})    # rows 0 and 1
+            dv = spr.Desc(**{**d.__dict__, "s_local": 2, "b": 1})
+            sub = {k: (v[rr] if k in ("x", "residual") else v) for k, v in inp.items()}
+            dev_in = {k: P.to_device(sub[k], w.io) for k in ("x", "residual")}
+            if V == "entry":
+                want = oracle.fwd(odv, None, None, sub["residual"], sub["gamma"],
+                                  sub["beta"] if ln else None)
+                g = spr.fwd(dv, None, None, dev_in["residual"], P.to_device(sub["gamma"]),
+                            P.to_device(sub["beta"]) if ln else None, write_h=False)
+                P.io_close("y", P.to_host(g["y"]), want["y"], w.io)
+            else:
+                want = oracle.fwd(odv, sub["x"], sub["bias"], sub["residual"], None, None)
+                g = spr.fwd(dv, dev_in["x"], P.to_device(sub["bias"]), dev_in["residual"],
+                            None, None)
+                P.exact("h", P.to_host(g["h"]), want["h"])
+                if want["mask"] is not None:
+                    P.exact("mask", P.to_host(g["mask"]), want["mask"])
+            print(f"[bench] {V} parity ok on rows [0, 1]", file=sys.stderr, flush=True)
+        elif K:
             ref_inp = dict(inp, x=oracle.reduce_parts(od, parts_host))
             got = P.gpu_fwd_rs(d, inp, parts_host, K)
         else:
             ref_inp = inp
             got = P.gpu_fwd(d, inp, store_mask=not args.no_mask)
-        rows = sorted({0, 1, w.rows // 2, w.rows - 1})
-        for r in rows:
-            sl, st = slice(r * w.h, (r + 1) * w.h), slice(r, r + 1)
-            want = P.oracle_fwd(od, ref_inp, rows=(r, r + 1))
-            if args.no_mask:
-                want["mask"] = None
-            P.check_fwd({k: (v[sl] if k in ("h", "y", "mask") else v[st]) if v is not None else None
-                         for k, v in got.items()}, want, w.io)
-        print(f"[bench] parity ok on rows {rows}", file=sys.stderr, flush=True)
+        if V == "full":
+            rows = sorted({0, 1, w.rows // 2, w.rows - 1})
+            for r in rows:
+                sl, st = slice(r * w.h, (r + 1) * w.h), slice(r, r + 1)
+                want = P.oracle_fwd(od, ref_inp, rows=(r, r + 1))
+                if args.no_mask:
+                    want["mask"] = None
+                P.check_fwd({k: (v[sl] if k in ("h", "y", "mask") else v[st])
+                             if v is not None else None for k, v in got.items()}, want, w.io)
+            print(f"[bench] parity ok on rows {rows}", file=sys.stderr, flush=True)
 
     # ---- device buffers: rotate sets so consecutive steps miss the MALL
     es = 2 if w.io == 1 else 4
@@ -279,7 +328,13 @@ def main():
     n_bwd = spr.sp_region_bwd_num_launches(d)
 
     def fwd(s, stream=stream):
-        if K:
+        if V == "entry":
+            spr.sp_region_fwd(d, None, None, s["res"], gamma, beta, None, s["y"], None,
+                              s["mean"], s["rstd"], stream)
+        elif V == "exit":
+            spr.sp_region_fwd(d, s["x"], bias, s["res"], None, None, s["h"], None, s["mask"],
+                              None, None, stream)
+        elif K:
             spr.sp_region_fwd_rs(d, s["parts"], K, bias, s["res"], gamma, beta, s["h"], s["y"],
                                  s["mask"], s["mean"], s["rstd"], stream)
         else:
@@ -287,11 +342,21 @@ def main():
                               s["mean"], s["rstd"], stream)
 
     def bwd_args(s):
+        if V == "entry":            # h is the residual; no x, so no dx and no dbias
+            return (s["dy"], None, s["res"], None, s["mean"], s["rstd"], gamma, None,
+                    s["b_dres"], s["b_dgamma"], s["b_dbeta"], None, s["b_workspace"])
         return (s["dy"], None, s["h"], s["mask"], s["mean"], s["rstd"], gamma, s["b_dx"],
                 s["b_dres"], s["b_dgamma"], s["b_dbeta"], s["b_dbias"], s["b_workspace"])
 
-    def bwd(s):
-        spr.sp_region_bwd(d, *bwd_args(s), stream)
+    def bwd(s, stream=stream):
+        if V == "exit":             # dh_out drawn as dy
+            spr.sp_region_bwd_exit(d, s["dy"], s["mask"], s["b_dx"], s["b_dbias"],
+                                   s["b_workspace"], stream)
+        else:
+            spr.sp_region_bwd(d, *bwd_args(s), stream)
+
+    if V == "exit":
+        n_bwd = 1                   # sp_region_bwd_exit: exit kernel + finalize
 
     for i in range(args.warmup):
         fwd(sets[i % nsets])
@@ -329,6 +394,8 @@ def main():
                 s = sets[i % nsets]
                 if k == 0:
                     fwd(s, stream=None)          # the capture stream
+                elif V == "exit":
+                    bwd(s, stream=None)
                 else:
                     spr.sp_region_bwd_launch(d, k - 1, *bwd_args(s))
         g = torch.cuda.CUDAGraph()
@@ -380,7 +447,7 @@ def main():
     # ---- layers of two calls (pre-attention and pre-MLP): call B's residual
     # is call A's h, and call A's backward takes call B's dresidual as dh_out
     layer = None
-    if w.calls_per_layer == 2:
+    if w.calls_per_layer == 2 and V == "full":
         def layer_step(sA, sB):
             spr.sp_region_fwd(dA, sA["x"], bias, sA["res"], gamma, beta, sA["h"], sA["y"],
                               sA["mask"], sA["mean"], sA["rstd"], stream)
@@ -410,13 +477,17 @@ def main():
                  "algorithmic_bytes": layer_bytes}
 
     # launch 0 is sp_region_fwd: its row kernel or its stream kernel
-    names = ["sp_region_fwd"] + (
+    names = ["sp_region_fwd"] + (["sp_region_bwd_exit"] if V == "exit" else
         ["sp_region_bwd_rows_kernel", "sp_region_bwd_finalize_kernel"] if n_bwd == 2 else
         ["sp_region_bwd_rowsum_kernel", "sp_region_bwd_main_kernel", "sp_region_bwd_finalize_kernel"])
     fwd_b, bwd_rows_b, bwd_grad_b = algorithmic_bytes(w, mask_stored=not args.no_mask,
                                                       x_parts=max(K, 1))
+    if V != "full":
+        fwd_b, bwd_rows_b = variant_bytes(w, V)
+        bwd_grad_b = 0
     # algorithmic bytes of each launch (the split path's row-sum pass only re-reads)
-    alg = [fwd_b] + ([bwd_rows_b, bwd_grad_b] if n_bwd == 2 else [0, bwd_rows_b, bwd_grad_b])
+    alg = [fwd_b] + ([bwd_rows_b] if V == "exit" else
+                     [bwd_rows_b, bwd_grad_b] if n_bwd == 2 else [0, bwd_rows_b, bwd_grad_b])
 
     tokens_per_s = w.rows / (ms_per_step / 1e3)
     total_alg = fwd_b + bwd_rows_b + bwd_grad_b
@@ -463,6 +534,9 @@ def main():
     if rs is not None:
         out["rs_prologue"] = rs
         out["config"]["rs_parts"] = K
+    if V != "full":
+        out["config"]["variant"] = {"entry": "norm-only entry (no x, p = 0)",
+                                    "exit": "norm-free exit (no norm)"}[V]
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w)

@@ -74,6 +74,8 @@ def lib():
         L.sp_region_fwd_rs.restype = ctypes.c_int
         L.sp_region_bwd.argtypes = [D] + [P] * 12 + [P, ctypes.c_size_t, P]
         L.sp_region_bwd.restype = ctypes.c_int
+        L.sp_region_bwd_exit.argtypes = [D, P, P, P, P, P, ctypes.c_size_t, P]
+        L.sp_region_bwd_exit.restype = ctypes.c_int
         L.sp_region_bwd_num_launches.argtypes = [D]
         L.sp_region_bwd_num_launches.restype = ctypes.c_int
         L.sp_region_bwd_launch.argtypes = [D, ctypes.c_int] + [P] * 12 + [P, ctypes.c_size_t, P]
@@ -141,13 +143,16 @@ def sp_region_fwd(d, x, bias, residual, gamma, beta, h_out, y_out, mask_out, mea
                   rstd_out, stream=None):
     import torch
     L = lib()
-    N, H, io, dev = d.rows, d.h, _io_dtype(d), x.device if x is not None else None
+    N, H, io = d.rows, d.h, _io_dtype(d)
+    dev = residual.device if residual is not None else None
     f32, u8 = torch.float32, torch.uint8
-    args = [_arg(x, "x", N * H, io, dev), _arg(bias, "bias", H, f32, dev, True),
-            _arg(residual, "residual", N * H, io, dev), _arg(gamma, "gamma", H, f32, dev),
-            _arg(beta, "beta", H, f32, dev, True), _arg(h_out, "h_out", N * H, io, dev),
-            _arg(y_out, "y_out", N * H, io, dev), _arg(mask_out, "mask_out", N * H, u8, dev, True),
-            _arg(mean_out, "mean_out", N, f32, dev, True), _arg(rstd_out, "rstd_out", N, f32, dev)]
+    args = [_arg(x, "x", N * H, io, dev, True), _arg(bias, "bias", H, f32, dev, True),
+            _arg(residual, "residual", N * H, io, dev), _arg(gamma, "gamma", H, f32, dev, True),
+            _arg(beta, "beta", H, f32, dev, True), _arg(h_out, "h_out", N * H, io, dev, True),
+            _arg(y_out, "y_out", N * H, io, dev, True),
+            _arg(mask_out, "mask_out", N * H, u8, dev, True),
+            _arg(mean_out, "mean_out", N, f32, dev, True),
+            _arg(rstd_out, "rstd_out", N, f32, dev, True)]
     st = L.sp_region_fwd(ctypes.byref(d.c()), *args, _stream(stream))
     if st != SPR_OK:
         raise SprError("sp_region_fwd", st)
@@ -183,7 +188,7 @@ def _bwd_args(d, dy, dh_out, h, mask, mean, rstd, gamma, dx_out, dres_out, dgamm
     return [_arg(dy, "dy", N * H, io, dev), _arg(dh_out, "dh_out", N * H, io, dev, True),
             _arg(h, "h", N * H, io, dev), _arg(mask, "mask", N * H, u8, dev, True),
             _arg(mean, "mean", N, f32, dev, True), _arg(rstd, "rstd", N, f32, dev),
-            _arg(gamma, "gamma", H, f32, dev), _arg(dx_out, "dx_out", N * H, io, dev),
+            _arg(gamma, "gamma", H, f32, dev), _arg(dx_out, "dx_out", N * H, io, dev, True),
             _arg(dres_out, "dres_out", N * H, io, dev),
             _arg(dgamma_out, "dgamma_out", H, f32, dev),
             _arg(dbeta_out, "dbeta_out", H, f32, dev, True),
@@ -200,6 +205,21 @@ def sp_region_bwd(d, dy, dh_out, h, mask, mean, rstd, gamma, dx_out, dres_out, d
         raise SprError("sp_region_bwd", st)
 
 
+def sp_region_bwd_exit(d, dh_out, mask, dx_out, dbias_out, workspace, stream=None):
+    """Backward of the norm-free exit (forward with gamma = None)."""
+    import torch
+    N, H, io, dev = d.rows, d.h, _io_dtype(d), dh_out.device if dh_out is not None else None
+    ws = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().sp_region_bwd_exit(ctypes.byref(d.c()), _arg(dh_out, "dh_out", N * H, io, dev),
+                                  _arg(mask, "mask", N * H, torch.uint8, dev, True),
+                                  _arg(dx_out, "dx_out", N * H, io, dev),
+                                  _arg(dbias_out, "dbias_out", H, torch.float32, dev, True),
+                                  ws, ctypes.c_size_t(ws_bytes), _stream(stream))
+    if st != SPR_OK:
+        raise SprError("sp_region_bwd_exit", st)
+
+
 def sp_region_bwd_num_launches(d):
     return int(lib().sp_region_bwd_num_launches(ctypes.byref(d.c())))
 
@@ -214,16 +234,18 @@ def sp_region_bwd_launch(d, index, dy, dh_out, h, mask, mean, rstd, gamma, dx_ou
 
 
 # ------------------------------------------------------------ allocation helpers
-def alloc_fwd_outputs(d, device, store_mask=True):
+def alloc_fwd_outputs(d, device, store_mask=True, norm=True, write_h=True):
     """torch.empty outputs of sp_region_fwd: h, y, mask, mean, rstd.  With
-    store_mask=False there is no mask (the backward regenerates it)."""
+    store_mask=False there is no mask (the backward regenerates it);
+    norm=False (the norm-free exit) has no y and statistics; write_h=False
+    (only for the norm-only entry) has no h."""
     import torch
     N, H, io = d.rows, d.h, _io_dtype(d)
     e = lambda n, dt: torch.empty(n, dtype=dt, device=device)
-    return {"h": e(N * H, io), "y": e(N * H, io),
+    return {"h": e(N * H, io) if write_h else None, "y": e(N * H, io) if norm else None,
             "mask": e(N * H, torch.uint8) if d.p > 0 and store_mask else None,
-            "mean": e(N, torch.float32) if d.norm == SPR_LAYERNORM else None,
-            "rstd": e(N, torch.float32)}
+            "mean": e(N, torch.float32) if norm and d.norm == SPR_LAYERNORM else None,
+            "rstd": e(N, torch.float32) if norm else None}
 
 
 def alloc_bwd_outputs(d, device, want_dbias=True):
@@ -238,9 +260,11 @@ def alloc_bwd_outputs(d, device, want_dbias=True):
             "workspace": torch.zeros(ws, dtype=torch.uint8, device=device)}
 
 
-def fwd(d, x, bias, residual, gamma, beta, stream=None, store_mask=True):
-    """Allocates the outputs and runs sp_region_fwd; returns them as a dict."""
-    o = alloc_fwd_outputs(d, x.device, store_mask)
+def fwd(d, x, bias, residual, gamma, beta, stream=None, store_mask=True, write_h=True):
+    """Allocates the outputs and runs sp_region_fwd; returns them as a dict.
+    x = None: the norm-only entry; gamma = None: the norm-free exit."""
+    o = alloc_fwd_outputs(d, residual.device, store_mask and x is not None, gamma is not None,
+                          write_h or x is not None)
     sp_region_fwd(d, x, bias, residual, gamma, beta, o["h"], o["y"], o["mask"], o["mean"],
                   o["rstd"], stream)
     return o

@@ -157,7 +157,7 @@ __global__ void __launch_bounds__(LB) sp_region_bwd_rows_kernel(BwdArgs a) {
             if (ok[k]) {
                 const int64_t off = rbase + (int64_t)vc[k] * E;
                 dres.store(static_cast<IO*>(a.dres_out) + off);
-                dx.store(static_cast<IO*>(a.dx_out) + off);
+                if (a.dx_out) dx.store(static_cast<IO*>(a.dx_out) + off);
             }
         }
     };
@@ -200,7 +200,7 @@ __global__ void __launch_bounds__(LB) sp_region_bwd_rows_kernel(BwdArgs a) {
         }
     }
 
-    float* part = a.partials + team * 3 * a.hidden;
+    float* part = a.partials + team * a.slots * a.hidden;
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
         if (ok[k]) {
@@ -229,7 +229,7 @@ __global__ void __launch_bounds__(256) sp_region_bwd_finalize_kernel(BwdArgs a) 
     __shared__ float4 part[kFinGroups][kFinCols / 4];
     const int lane = threadIdx.x % (kFinCols / 4), q = threadIdx.x / (kFinCols / 4);
     const int64_t j = (int64_t)blockIdx.x * kFinCols + lane * 4;
-    const int64_t n3 = 3 * a.hidden;
+    const int64_t n3 = (int64_t)a.slots * a.hidden;
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
     if (j < n3) {
         // Group q's teams q, q+16, ... in order, four loads in flight at a
@@ -267,7 +267,8 @@ __global__ void __launch_bounds__(256) sp_region_bwd_finalize_kernel(BwdArgs a) 
         }
         const int k = (int)(j / a.hidden);
         const int64_t c = j - (int64_t)k * a.hidden;
-        float* out = k == 0 ? a.dgamma_out : (k == 1 ? a.dbeta_out : a.dbias_out);
+        float* out = a.slots == 1 ? a.dbias_out
+                                  : (k == 0 ? a.dgamma_out : (k == 1 ? a.dbeta_out : a.dbias_out));
         if (out) *reinterpret_cast<float4*>(out + c) = t;
     }
 }
@@ -341,7 +342,7 @@ __global__ void __launch_bounds__(LB) sp_region_bwd_rowsum_kernel(BwdArgs a) {
 }
 
 // Adds the 4 waves' column partials in wave order and writes them as
-// partial row `slot` of row block blockIdx.y: colpart[(rb*3 + slot)*h + c].
+// partial row `slot` of row block blockIdx.y: colpart[(rb*slots + slot)*h + c].
 template <int E>
 __device__ __forceinline__ void split_store_colpart(const BwdArgs& a, float (*sh)[64][E],
                                                     const float (&acc)[E], int slot, int vec,
@@ -357,7 +358,8 @@ __device__ __forceinline__ void split_store_colpart(const BwdArgs& a, float (*sh
         for (int w = 1; w < kSplitWaves; ++w)
 #pragma unroll
             for (int j = 0; j < E; ++j) t[j] += sh[w][lane][j];
-        float* out = a.partials + ((int64_t)blockIdx.y * 3 + slot) * a.hidden + (int64_t)vec * E;
+        float* out = a.partials + ((int64_t)blockIdx.y * a.slots + slot) * a.hidden +
+                     (int64_t)vec * E;
 #pragma unroll
         for (int j = 0; j < E; j += 4)
             *reinterpret_cast<float4*>(out + j) = make_float4(t[j], t[j + 1], t[j + 2], t[j + 3]);
@@ -460,7 +462,7 @@ __global__ void __launch_bounds__(256) sp_region_bwd_main_kernel(BwdArgs a) {
             if (ok && rok) {
                 const int64_t off = row * a.hidden + (int64_t)vec * E;
                 dres.store(static_cast<IO*>(a.dres_out) + off);
-                dx.store(static_cast<IO*>(a.dx_out) + off);
+                if (a.dx_out) dx.store(static_cast<IO*>(a.dx_out) + off);
             }
         }
         cur = nxt;
@@ -468,6 +470,114 @@ __global__ void __launch_bounds__(256) sp_region_bwd_main_kernel(BwdArgs a) {
     split_store_colpart<E>(a, sh, acc_g, 0, vec, ok);
     split_store_colpart<E>(a, sh, acc_b, 1, vec, ok);
     split_store_colpart<E>(a, sh, acc_x, 2, vec, ok);
+}
+
+// ---------------------------------------------------------------- norm-free exit
+// Backward of h = residual + dropout(x + bias) alone (no norm after it):
+// dh = dh_out, so dx = keep ? dh_out * scale : 0, dbias = sum over rows of
+// dx, and dresidual is dh_out itself (not written).  Tiles as the split
+// path's second pass (tile_rows rows x one wave's 64 vectors, 4 waves taking
+// rows w, w + 4, ..., U rows per group loaded ahead); the tile's dbias
+// partial is added across the waves in wave order into slot 0 of its row
+// block.
+template <int U, int MW>
+struct ExitIn {
+    uint4 dho[U];
+    uint32_t mask[U][MW];
+};
+
+template <typename IO, int DROP>
+__global__ void __launch_bounds__(256) sp_region_bwd_exit_kernel(BwdArgs a) {
+    using V = Vec<IO>;
+    constexpr int E = V::N, U = kSplitUnroll, MW = E / 4;
+    __shared__ float sh[kSplitWaves][64][E];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int vec = blockIdx.x * 64 + lane;
+    const bool ok = vec < a.nvec;
+    const int vcl = ok ? vec : a.nvec - 1;
+    float acc[E];
+#pragma unroll
+    for (int j = 0; j < E; ++j) acc[j] = 0.0f;
+
+    const int64_t r0 = (int64_t)blockIdx.y * a.tile_rows;
+    const int64_t r1 = r0 + a.tile_rows < a.rows ? r0 + a.tile_rows : a.rows;
+    constexpr int64_t step = kSplitWaves * U;
+
+    auto load_group = [&](int64_t base, ExitIn<U, MW>& in) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t row = base + kSplitWaves * u;
+            const int64_t rc = row < r1 ? row : r1 - 1;          // clamp: always a valid row
+            const int64_t off = rc * a.hidden + (int64_t)vcl * E;
+            in.dho[u] = load_stream(static_cast<const IO*>(a.dh_out) + off);
+            if (DROP == kDropMask) {
+#pragma unroll
+                for (int w = 0; w < MW; ++w)
+                    in.mask[u][w] = __builtin_nontemporal_load(
+                        reinterpret_cast<const uint32_t*>(a.mask + off) + w);
+            }
+        }
+    };
+
+    ExitIn<U, MW> cur, nxt;
+    int64_t base = r0 + wave;
+    if (base < r1) load_group(base, cur);
+    for (; base < r1; base += step) {
+        if (base + step < r1) load_group(base + step, nxt);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t row = base + kSplitWaves * u;
+            const bool rok = row < r1;                       // wave-uniform
+            V dho, dx;
+            dho.set(cur.dho[u]);
+            uint32_t kb = 0xffu;
+            if (DROP == kDropMask) {
+                kb = MaskBytes<4>::from_word(cur.mask[u][0]);
+                if (MW == 2) kb |= MaskBytes<4>::from_word(cur.mask[u][MW - 1]) << 4;
+            } else if (DROP == kDropRegen) {
+                kb = keep_bits<E>((a.row_base + (uint64_t)(rok ? row : r1 - 1)) *
+                                          (uint64_t)a.hidden + (uint64_t)vcl * E,
+                                  a.off_lo, a.off_hi, a.key_lo, a.key_hi, a.thr);
+            }
+#pragma unroll
+            for (int j = 0; j < E; ++j) {
+                const float dh = dho.v[j];
+                const float dxu =
+                    DROP != kDropNone ? (((kb >> j) & 1u) ? dh * a.scale : 0.0f) : dh;
+                dx.v[j] = dxu;
+                if (ok && rok) acc[j] += dxu;
+            }
+            if (ok && rok) dx.store(static_cast<IO*>(a.dx_out) + row * a.hidden + (int64_t)vec * E);
+        }
+        cur = nxt;
+    }
+    if (a.dbias_out) split_store_colpart<E>(a, sh, acc, 0, vec, ok);
+}
+
+static hipError_t launch_finalize(const BwdArgs& a, hipStream_t s);
+
+hipError_t launch_bwd_exit(const spr_desc& d, const BwdPlan& p, const BwdArgs& a, hipStream_t s) {
+    const dim3 g((unsigned)p.col_tiles, (unsigned)p.row_blocks), b(256);
+    const int mode = !(d.p > 0.0f) ? kDropNone : (a.mask ? kDropMask : kDropRegen);
+    if (d.io == SPR_BF16) {
+        if (mode == kDropMask)
+            hipLaunchKernelGGL((sp_region_bwd_exit_kernel<__bf16, kDropMask>), g, b, 0, s, a);
+        else if (mode == kDropRegen)
+            hipLaunchKernelGGL((sp_region_bwd_exit_kernel<__bf16, kDropRegen>), g, b, 0, s, a);
+        else
+            hipLaunchKernelGGL((sp_region_bwd_exit_kernel<__bf16, kDropNone>), g, b, 0, s, a);
+    } else {
+        if (mode == kDropMask)
+            hipLaunchKernelGGL((sp_region_bwd_exit_kernel<float, kDropMask>), g, b, 0, s, a);
+        else if (mode == kDropRegen)
+            hipLaunchKernelGGL((sp_region_bwd_exit_kernel<float, kDropRegen>), g, b, 0, s, a);
+        else
+            hipLaunchKernelGGL((sp_region_bwd_exit_kernel<float, kDropNone>), g, b, 0, s, a);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !a.dbias_out) return e;
+    return launch_finalize(a, s);
 }
 
 // Teams: one workgroup per CU (fewer workgroups cannot draw the full HBM
@@ -514,7 +624,7 @@ static hipError_t bwd_by_vpt(const RowPlan& p, const BwdArgs& a, hipStream_t s) 
 }
 
 static hipError_t launch_finalize(const BwdArgs& a, hipStream_t s) {
-    const int64_t n3 = 3 * a.hidden;
+    const int64_t n3 = (int64_t)a.slots * a.hidden;
     hipLaunchKernelGGL(sp_region_bwd_finalize_kernel, dim3((unsigned)((n3 + kFinCols - 1) / kFinCols)),
                        dim3(256), 0, s, a);
     return hipGetLastError();

@@ -41,6 +41,22 @@ __device__ __forceinline__ float fwd_dropout_residual(const FwdArgs& a, int64_t 
     constexpr int E = Vec<IO>::N;
     constexpr int MW = E / 4;                 // mask words per vector
     const int64_t rbase = row * a.hidden;
+    if (!a.x) {                               // norm-only entry: h is the residual, bit for bit
+        float sum = 0.0f;
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) {
+            Vec<IO> r;
+            r.set(rq[k]);
+#pragma unroll
+            for (int j = 0; j < E; ++j) hv[k][j] = r.v[j];
+            if (ok[k]) {
+#pragma unroll
+                for (int j = 0; j < E; ++j) sum += hv[k][j];
+                if (a.h_out) store_stream(static_cast<IO*>(a.h_out) + rbase + (int64_t)vc[k] * E, rq[k]);
+            }
+        }
+        return sum;
+    }
     bool keep[VPT][E];
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
@@ -165,7 +181,8 @@ __device__ __forceinline__ void load_x_res(const FwdArgs& a, int64_t row, const 
     const int64_t rbase = row * a.hidden;
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
-        xq[k] = load_stream(static_cast<const IO*>(a.x) + rbase + (int64_t)vc[k] * E);
+        xq[k] = a.x ? load_stream(static_cast<const IO*>(a.x) + rbase + (int64_t)vc[k] * E)
+                    : make_uint4(0u, 0u, 0u, 0u);
         rq[k] = load_stream(static_cast<const IO*>(a.residual) + rbase + (int64_t)vc[k] * E);
     }
 }
@@ -293,6 +310,7 @@ __global__ void __launch_bounds__(LB) sp_region_fwd_kernel(FwdArgs a) {
 
     float hv[VPT][E];
     const float sum = fwd_dropout_residual<IO, DROP, VPT>(a, row, vc, ok, xq, rq, bb, hv);
+    if (!a.gamma) return;                // norm-free exit: h and the mask only (uniform)
 
     float g[VPT][E], bt[VPT][E];
     load_affine<NORM, VPT, E>(a, vc, g, bt);
@@ -327,11 +345,12 @@ __global__ void __launch_bounds__(LB) sp_region_fwd_stream_kernel(FwdArgs a) {
     load_x_res<IO, VPT>(a, row, vc, xa, ra);
     float bb[VPT][E], g[VPT][E], bt[VPT][E];
     load_bias<VPT, E>(a, vc, bb);
-    load_affine<NORM, VPT, E>(a, vc, g, bt);
+    if (a.gamma) load_affine<NORM, VPT, E>(a, vc, g, bt);
 
     auto one_row = [&](int64_t r, const uint4 (&xq)[VPT], const uint4 (&rq)[VPT], float* slot) {
         float hv[VPT][E];
         const float sum = fwd_dropout_residual<IO, DROP, VPT>(a, r, vc, ok, xq, rq, bb, hv);
+        if (!a.gamma) return;            // norm-free exit (uniform)
         float mean, rstd;
         fwd_stats<NORM, VPT, E>(a, ok, hv, sum, slot, nwaves, mean, rstd);
         fwd_store_y<IO, NORM, VPT>(a, r, tid, vc, ok, hv, g, bt, mean, rstd);

@@ -122,6 +122,7 @@ struct BwdArgs {
     int teams;             // row teams in the grid = partial rows
     int col_tiles;         // split path: tiles of one wave's 64 vectors across a row
     int tile_rows;         // split path: rows per tile
+    int slots;             // partial rows per team: 3 (dgamma, dbeta, dbias) or 1 (dbias)
 };
 
 // The backward's two strategies.
@@ -154,6 +155,10 @@ hipError_t launch_fwd(const spr_desc& d, const RowPlan& plan, const FwdArgs& a, 
 
 // Number of row teams (= fp32 partial rows) the fused backward uses.
 int64_t bwd_teams(const spr_desc& d, const RowPlan& plan);
+// The norm-free exit's backward: dx = keep ? dh_out * scale : 0 over the
+// split path's tiles, then (with dbias) the finalize over one slot.
+hipError_t launch_bwd_exit(const spr_desc& d, const BwdPlan& plan, const BwdArgs& a,
+                           hipStream_t s);
 // Runs launches [first, last) of the backward's sequence.
 hipError_t launch_bwd(const spr_desc& d, const BwdPlan& plan, const BwdArgs& a, hipStream_t s,
                       int first, int last);

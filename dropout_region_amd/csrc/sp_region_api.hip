@@ -223,8 +223,18 @@ spr_status fwd_impl(const spr_desc* d, const void* x, int nparts, const float* b
     spr_status st = check_desc(d, &plan, kPlanForward);
     if (st != SPR_OK) return st;
     const bool ln = d->norm == SPR_LAYERNORM, drop = d->p > 0.0f;
-    if (!x || !residual || !gamma || !h_out || !y_out || !rstd_out) return SPR_ERR_INVALID_ARG;
-    if (ln != (beta != nullptr) || ln != (mean_out != nullptr)) return SPR_ERR_INVALID_ARG;
+    if (!residual || (!x && !gamma)) return SPR_ERR_INVALID_ARG;
+    if (x) {                             // the branch: x (+ bias), dropout, residual add
+        if (!h_out) return SPR_ERR_INVALID_ARG;
+    } else {                             // norm-only entry: h is the residual
+        if (drop || bias || nparts != 1) return SPR_ERR_INVALID_ARG;
+    }
+    if (gamma) {                         // the norm
+        if (!y_out || !rstd_out) return SPR_ERR_INVALID_ARG;
+        if (ln != (beta != nullptr) || ln != (mean_out != nullptr)) return SPR_ERR_INVALID_ARG;
+    } else {                             // norm-free exit: h and the mask only
+        if (beta || y_out || mean_out || rstd_out) return SPR_ERR_INVALID_ARG;
+    }
     if (!drop) mask_out = nullptr;                                   // ignored at p == 0
     const void* io16[] = {x, residual, h_out, y_out};
     for (const void* p : io16)
@@ -309,7 +319,7 @@ spr_status sp_region_fwd_rs(const spr_desc* d, const void* x_parts, int32_t npar
                             const float* bias, const void* residual, const float* gamma,
                             const float* beta, void* h_out, void* y_out, uint8_t* mask_out,
                             float* mean_out, float* rstd_out, hipStream_t stream) {
-    if (nparts < 1 || nparts > kMaxParts) return SPR_ERR_INVALID_ARG;
+    if (!x_parts || nparts < 1 || nparts > kMaxParts) return SPR_ERR_INVALID_ARG;
     return fwd_impl(d, x_parts, nparts, bias, residual, gamma, beta, h_out, y_out, mask_out,
                     mean_out, rstd_out, stream);
 }
@@ -330,7 +340,7 @@ spr_status prepare_bwd(const spr_desc* d, const void* dy, const void* dh_out, co
     BwdPlan plan;
     if (!make_bwd_plan(*d, &plan)) return SPR_ERR_UNSUPPORTED;
     const bool ln = d->norm == SPR_LAYERNORM, drop = d->p > 0.0f;
-    if (!dy || !h || !rstd || !gamma || !dx_out || !dres_out || !dgamma_out)
+    if (!dy || !h || !rstd || !gamma || !dres_out || !dgamma_out)   // dx_out: optional
         return SPR_ERR_INVALID_ARG;
     if (ln != (mean != nullptr) || ln != (dbeta_out != nullptr)) return SPR_ERR_INVALID_ARG;
     if (!drop) mask = nullptr;          // p > 0 without a mask: regenerated
@@ -372,6 +382,7 @@ spr_status prepare_bwd(const spr_desc* d, const void* dy, const void* dh_out, co
     a.teams = (int)(split ? plan.row_blocks : plan.teams);
     a.col_tiles = plan.col_tiles;
     a.tile_rows = plan.tile_rows;
+    a.slots = 3;
     *plan_out = plan;
     *args_out = a;
     return SPR_OK;
@@ -417,6 +428,45 @@ spr_status sp_region_bwd_launch(const spr_desc* d, int index, const void* dy, co
     if (st != SPR_OK) return st;
     if (index < 0 || index >= bwd_num_launches(plan)) return SPR_ERR_INVALID_ARG;
     return launch_bwd(*d, plan, a, stream, index, index + 1) == hipSuccess ? SPR_OK : SPR_ERR_HIP;
+}
+
+spr_status sp_region_bwd_exit(const spr_desc* d, const void* dh_out, const uint8_t* mask,
+                              void* dx_out, float* dbias_out, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+    RowPlan rp;
+    spr_status st = check_desc(d, &rp, kPlanBackward);
+    if (st != SPR_OK) return st;
+    BwdPlan plan;
+    if (!make_bwd_plan(*d, &plan)) return SPR_ERR_UNSUPPORTED;
+    if (!dh_out || !dx_out) return SPR_ERR_INVALID_ARG;
+    if (!(d->p > 0.0f)) mask = nullptr;
+    if (!aligned(dh_out, 16) || !aligned(dx_out, 16) || !aligned(mask, 8) ||
+        !aligned(dbias_out, 4))
+        return SPR_ERR_INVALID_ARG;
+    const int64_t rows = d->s_local * d->b;
+    const uint64_t E = (uint64_t)rows * (uint64_t)d->h;
+    const uint64_t es = (d->io == SPR_BF16) ? 2u : 4u;
+    // slot 0 of [row_blocks][1][h] fp32 column partials
+    const size_t need = dbias_out ? (size_t)plan.row_blocks * (size_t)d->h * sizeof(float) : 0;
+    if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 16)))
+        return SPR_ERR_WORKSPACE;
+    const Range outs[] = {range_of(dx_out, E * es), range_of(dbias_out, (uint64_t)d->h * 4u),
+                          range_of(need ? workspace : nullptr, need)};
+    const Range ins[] = {range_of(dh_out, E * es), range_of(mask, E)};
+    if (!disjoint(outs, 3, ins, 2)) return SPR_ERR_INVALID_ARG;
+
+    BwdArgs a{};
+    a.dh_out = dh_out; a.mask = mask; a.dx_out = dx_out; a.dbias_out = dbias_out;
+    a.partials = static_cast<float*>(workspace);
+    a.rows = rows;
+    a.hidden = d->h;
+    set_dropout(*d, rows, &a);
+    a.nvec = plan.rows.nvec;
+    a.teams = (int)plan.row_blocks;
+    a.col_tiles = plan.col_tiles;
+    a.tile_rows = plan.tile_rows;
+    a.slots = 1;
+    return launch_bwd_exit(*d, plan, a, stream) == hipSuccess ? SPR_OK : SPR_ERR_HIP;
 }
 
 }  // extern "C"

@@ -124,7 +124,19 @@ typedef struct {
  *  mean_out [N]  fp32  LayerNorm: required; RMSNorm: must be NULL
  *  rstd_out [N]  fp32  1/sqrt(var + eps) (LayerNorm) or 1/sqrt(mean(h^2)+eps)
  * h_out and mask_out are bit-exact functions of the inputs; y and the
- * statistics are computed in fp32. */
+ * statistics are computed in fp32.
+ *
+ * The two ends of the layer stack ("Tensor and sequence parallelism --
+ * explained with pictures", section "Transformer block": a sub-block has a
+ * LayerNorm at its entrance and a dropout and residual add at its exit):
+ *  - x == NULL, the norm-only entry (the first block's norm, with no
+ *    branch before it): h is the residual bit for bit and y = Norm(residual).
+ *    p must be 0 and bias NULL; h_out may be NULL (h is then not written:
+ *    the caller's residual is h, and the backward reads it as h).
+ *  - gamma == NULL, the norm-free exit (the last residual add, with no norm
+ *    after it): only h and the mask are written; beta, y_out, mean_out and
+ *    rstd_out must be NULL.  Its backward is sp_region_bwd_exit.
+ * x and gamma may not both be NULL. */
 spr_status sp_region_fwd(const spr_desc* desc,
                          const void* x, const float* bias, const void* residual,
                          const float* gamma, const float* beta,
@@ -172,7 +184,8 @@ size_t sp_region_bwd_workspace_bytes(const spr_desc* desc);
  *                         from desc's seed, offset, shard_index and t --
  *                         the desc must then be the forward's)
  *  gamma       [h]  fp32
- *  dx_out      [N,h] io   gradient of x
+ *  dx_out      [N,h] io   gradient of x; may be NULL (not written: the
+ *                         norm-only entry has no x)
  *  dres_out    [N,h] io   gradient of residual (= gradient of h)
  *  dgamma_out  [h]  fp32  this shard's partial sum over its N rows
  *  dbeta_out   [h]  fp32  LayerNorm: required; RMSNorm: must be NULL
@@ -192,6 +205,23 @@ spr_status sp_region_bwd(const spr_desc* desc,
                          float* dgamma_out, float* dbeta_out, float* dbias_out,
                          void* workspace, size_t workspace_bytes,
                          hipStream_t stream);
+
+/* Backward of the norm-free exit (a forward with gamma == NULL):
+ * dh = dh_out, so
+ *  dh_out     [N,h] io   gradient of h (required)
+ *  mask       as written by the forward (NULL when p == 0; with p > 0, NULL
+ *             regenerates the decisions as in sp_region_bwd)
+ *  dx_out     [N,h] io   keep ? dh_out * scale : 0
+ *  dbias_out  [h]  fp32  this shard's partial sum of dx over its rows; may be
+ *                        NULL (then no workspace is needed)
+ *  workspace  at least sp_region_bwd_workspace_bytes(desc) bytes when
+ *             dbias_out is given
+ * The gradient of the residual is dh_out itself and is not written.  Same
+ * conventions and checks as sp_region_bwd. */
+spr_status sp_region_bwd_exit(const spr_desc* desc, const void* dh_out, const uint8_t* mask,
+                              void* dx_out, float* dbias_out,
+                              void* workspace, size_t workspace_bytes,
+                              hipStream_t stream);
 
 /* The backward is a fixed sequence of kernel launches on `stream`: the row
  * pass(es), then a fixed-order column finalize of the parameter gradients.

@@ -273,7 +273,7 @@ int spo_fwd(const spo_desc* d, int64_t r0, int64_t r1,
     if (x) {                                   /* the branch: x (+ bias), dropout */
         if (!h_out || (d->p > 0.0f && !mask_out)) return -1;
     } else {                                   /* norm-only entry: h is the residual */
-        if (bias || mask_out) return -1;
+        if (bias || mask_out || d->p > 0.0f) return -1;
     }
     if (gamma) {                               /* the norm */
         if (!y_out || !rstd_out) return -1;

@@ -90,8 +90,8 @@ int spo_reduce_parts(const spo_desc* d, int nparts, const void* parts, void* x_o
  * Two variants at the ends of the layer stack (a block boundary with no
  * branch before the first LayerNorm, and none after the last residual add):
  *  - x == NULL, the norm-only entry: no branch, h is the residual bit for
- *    bit (no add), y = Norm(residual); bias and mask_out must be NULL, h_out
- *    may be NULL (then h is not written);
+ *    bit (no add), y = Norm(residual); p must be 0, bias and mask_out NULL,
+ *    h_out may be NULL (then h is not written);
  *  - gamma == NULL, the norm-free exit: h and the mask only; beta, y_out,
  *    mean_out and rstd_out must be NULL.
  * Returns 0 on success, -1 on an invalid argument.

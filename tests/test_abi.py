@@ -30,6 +30,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["sp_region_fwd", "sp_region_fwd_rs", "sp_region_bwd",
+                            "sp_region_bwd_exit",
                             "sp_region_bwd_workspace_bytes",
                             "sp_region_bwd_num_launches", "sp_region_bwd_launch",
                             "sp_region_activation_bytes", "sp_region_status_string"])
@@ -92,6 +93,33 @@ def test_fwd_rs_checks(L):
     bad[5] = FWD_OK[0] + 3 * 1024                # h_out inside slab 3 of 4
     assert _fwd_rs_raw(L, d, 4, bad) == spr.SPR_ERR_INVALID_ARG
     assert _fwd_rs_raw(L, _good_desc(h=60), 4, FWD_OK) == spr.SPR_ERR_UNSUPPORTED
+
+
+def test_variant_rules(L):
+    d0 = _good_desc(p=0.0)
+    entry = list(FWD_OK)
+    entry[0] = 0                                 # no x ...
+    assert _fwd_raw(L, _good_desc(), entry, ) == spr.SPR_ERR_INVALID_ARG   # ... with p > 0
+    assert _fwd_raw(L, d0, entry) == spr.SPR_ERR_INVALID_ARG              # ... with a bias
+    both = list(entry)
+    both[1] = 0
+    both[3] = 0                                  # neither x nor gamma
+    assert _fwd_raw(L, d0, both) == spr.SPR_ERR_INVALID_ARG
+    exit_ = list(FWD_OK)
+    exit_[3] = 0                                 # no gamma, but y/beta/mean/rstd given
+    assert _fwd_raw(L, d0, exit_) == spr.SPR_ERR_INVALID_ARG
+    exit_[4] = exit_[6] = exit_[8] = 0
+    assert _fwd_raw(L, d0, exit_) == spr.SPR_ERR_INVALID_ARG              # rstd still given
+    exit_[5] = 0
+    exit_[9] = 0                                 # ... and no h_out
+    assert _fwd_raw(L, d0, exit_) == spr.SPR_ERR_INVALID_ARG
+    call = lambda dho, dx, ws, n: L.sp_region_bwd_exit(
+        ctypes.byref(d0), ctypes.c_void_p(dho), None, ctypes.c_void_p(dx),
+        ctypes.c_void_p(A + 0x300000), ctypes.c_void_p(ws), ctypes.c_size_t(n), None)
+    assert call(0, A + 0x100000, A + 0x200000, 1 << 20) == spr.SPR_ERR_INVALID_ARG  # no dh_out
+    assert call(A, 0, A + 0x200000, 1 << 20) == spr.SPR_ERR_INVALID_ARG            # no dx_out
+    assert call(A, A + 0x100000, 0, 0) == spr.SPR_ERR_WORKSPACE                    # dbias, no ws
+    assert call(A, A, A + 0x200000, 1 << 20) == spr.SPR_ERR_INVALID_ARG            # dx aliases
 
 
 def test_fwd_pointer_rules(L):

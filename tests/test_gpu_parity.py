@@ -166,6 +166,105 @@ def test_reduce_scatter_prologue(name):
             P.exact(f"{k} (fused prologue vs summed x)", got[k], plain[k])
 
 
+# The two ends of the layer stack: the norm-only entry (no x: h is the
+# residual) and the norm-free exit (no gamma: h and the mask only).
+ENTRY = {
+    "bf16_ln_h6144": base(s_local=16, b=4, h=6144, p=0.0),
+    "fp32_rms_h3076_ragged": base(s_local=6, b=2, h=3076, io=F32, norm=RMS, p=0.0, eps=1e-6),
+    "bf16_ln_h1000_wave_rows": base(s_local=37, b=1, h=1000, p=0.0),
+    "bf16_rms_h8192_1100_rows": base(s_local=1100, b=1, h=8192, norm=RMS, p=0.0, eps=1e-6),
+    "bf16_ln_h25600": base(s_local=3, b=2, h=25600, p=0.0),
+}
+
+
+@pytest.mark.parametrize("name", sorted(ENTRY))
+def test_norm_only_entry(name):
+    import torch
+    d, od = descs(**ENTRY[name])
+    _say(f"[case] norm-only entry {name}: {ENTRY[name]}")
+    inp = make_inputs(d.rows, d.h, d.io, seed=zlib.crc32(name.encode()) % 1000, dh_out=True)
+    ln = d.norm == LN
+    want = oracle.fwd(od, None, None, inp["residual"], inp["gamma"], inp["beta"] if ln else None)
+    res = P.to_device(inp["residual"], d.io)
+    gam, bet = P.to_device(inp["gamma"]), P.to_device(inp["beta"]) if ln else None
+    for fpath in (None, "rows", "stream"):
+        with P._env("SPR_FWD_PATH", fpath):
+            o = spr.fwd(d, None, None, res, gam, bet, write_h=False)
+            oh = spr.fwd(d, None, None, res, gam, bet, write_h=True)
+        got = {k: P.to_host(v) for k, v in o.items()}
+        assert got["h"] is None and got["mask"] is None
+        P.io_close("y", got["y"], want["y"], d.io)
+        if ln:
+            P.stats_close("mean", got["mean"], want["mean"])
+        P.stats_close("rstd", got["rstd"], want["rstd"])
+        P.exact("h (entry) = residual", P.to_host(oh["h"]), inp["residual"])
+        for k in ("y", "mean", "rstd"):
+            if got[k] is not None:
+                P.exact(f"{k} (with and without h)", P.to_host(oh[k]), got[k])
+    wb = oracle.bwd(od, inp["dy"], inp["dh_out"], inp["residual"], None, want["mean"],
+                    want["rstd"], inp["gamma"], want_dbias=False, want_dx=False)
+    for path in ("fused", "split"):
+        with P._env("SPR_BWD_PATH", path):
+            b = spr.alloc_bwd_outputs(d, res.device, want_dbias=False)
+            spr.sp_region_bwd(d, P.to_device(inp["dy"], d.io), P.to_device(inp["dh_out"], d.io),
+                              res, None, P.to_device(want["mean"]), P.to_device(want["rstd"]),
+                              gam, None, b["dres"], b["dgamma"], b["dbeta"], None,
+                              b["workspace"])
+            torch.cuda.synchronize()
+        P.io_close(f"dres ({path})", P.to_host(b["dres"]), wb["dres"], d.io)
+        P.param_grad_close(f"dgamma ({path})", P.to_host(b["dgamma"]), wb["dgamma"])
+        if ln:
+            P.param_grad_close(f"dbeta ({path})", P.to_host(b["dbeta"]), wb["dbeta"])
+
+
+EXIT = {
+    "bf16_h6144_p0.1_shard2of4": base(s_local=16, b=4, h=6144, shard_index=2, t=4),
+    "fp32_h260_ragged_p0.3": base(s_local=13, b=3, h=260, io=F32, p=0.3),
+    "bf16_h25600_p0": base(s_local=3, b=2, h=25600, p=0.0),
+    "bf16_h8192_1100_rows": base(s_local=1100, b=1, h=8192, offset=5),
+    "fp32_h4_single_vector": base(s_local=9, b=1, h=4, io=F32, p=0.5),
+}
+
+
+@pytest.mark.parametrize("name", sorted(EXIT))
+def test_norm_free_exit(name):
+    import torch
+    d, od = descs(**EXIT[name])
+    _say(f"[case] norm-free exit {name}: {EXIT[name]}")
+    inp = make_inputs(d.rows, d.h, d.io, seed=zlib.crc32(name.encode()) % 1000, dh_out=True)
+    want = oracle.fwd(od, inp["x"], inp["bias"], inp["residual"], None, None)
+    x, res = P.to_device(inp["x"], d.io), P.to_device(inp["residual"], d.io)
+    bias = P.to_device(inp["bias"])
+    for fpath in (None, "rows", "stream"):
+        with P._env("SPR_FWD_PATH", fpath):
+            o = spr.fwd(d, x, bias, res, None, None)
+        got = {k: P.to_host(v) for k, v in o.items()}
+        for k in ("y", "mean", "rstd"):
+            assert got[k] is None
+        P.exact("h (exit)", got["h"], want["h"])
+        if want["mask"] is not None:
+            P.exact("mask (exit)", got["mask"], want["mask"])
+    wb = oracle.bwd(od, None, inp["dh_out"], None, want["mask"], None, None, None,
+                    want_dres=False)
+    dho = P.to_device(inp["dh_out"], d.io)
+    results = []
+    for mask in ((want["mask"], None) if d.p > 0 else (None,)):
+        for with_dbias in (True, False):
+            dx = torch.empty_like(dho)
+            dbias = torch.empty(d.h, dtype=torch.float32, device=dho.device) if with_dbias else None
+            ws = torch.zeros(max(spr.sp_region_bwd_workspace_bytes(d), 16), dtype=torch.uint8,
+                             device=dho.device) if with_dbias else None
+            spr.sp_region_bwd_exit(d, dho, P.to_device(mask), dx, dbias, ws)
+            torch.cuda.synchronize()
+            gdx = P.to_host(dx)
+            P.io_close("dx (exit)", gdx, wb["dx"], d.io)
+            if with_dbias:
+                P.param_grad_close("dbias (exit)", P.to_host(dbias), wb["dbias"])
+            results.append(gdx)
+    for r in results[1:]:
+        P.exact("dx (exit; mask stored vs regenerated, dbias or not)", r, results[0])
+
+
 @pytest.mark.parametrize("with_bias,with_dh_out,want_dbias", [(False, False, True),
                                                               (True, False, False),
                                                               (False, True, False)])

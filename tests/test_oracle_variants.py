@@ -124,5 +124,8 @@ def test_variant_argument_rules(olib):
     inp = make_inputs(d.rows, d.h, F32, seed=45)
     with pytest.raises(ValueError):            # neither branch nor norm
         oracle.fwd(d, None, None, inp["residual"], None, None, L=olib)
+    with pytest.raises(ValueError):            # entry with dropout (no branch to drop)
+        oracle.fwd(d, None, None, inp["residual"], inp["gamma"], inp["beta"], L=olib)
+    d0 = oracle.Desc(s_local=2, b=1, h=8, io=F32, norm=LN, p=0.0)
     with pytest.raises(ValueError):            # entry with a bias
-        oracle.fwd(d, None, inp["bias"], inp["residual"], inp["gamma"], inp["beta"], L=olib)
+        oracle.fwd(d0, None, inp["bias"], inp["residual"], inp["gamma"], inp["beta"], L=olib)
