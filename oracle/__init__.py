@@ -83,6 +83,8 @@ def load(path):
     L.spo_f32_to_bf16.restype = ctypes.c_uint16
     L.spo_bf16_to_f32.argtypes = [ctypes.c_uint16]
     L.spo_bf16_to_f32.restype = ctypes.c_float
+    L.spo_attention.argtypes = [ctypes.POINTER(spo_attn_desc), P, P, P, P, P]
+    L.spo_attention.restype = ctypes.c_int
     L.spo_reduce_parts.argtypes = [D, ctypes.c_int, P, P]
     L.spo_reduce_parts.restype = ctypes.c_int
     L.spo_fwd.argtypes = [D, I64, I64] + [P] * 10
@@ -148,6 +150,46 @@ def f32_to_bf16(values, L=None):
 def bf16_to_f32(bits):
     """Exact widening of raw bf16 patterns (a shift; no rounding involved)."""
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+# ---------------------------------------------------------------- ring attention
+class spo_attn_desc(ctypes.Structure):
+    _fields_ = [("s_local", ctypes.c_int64), ("b", ctypes.c_int64), ("heads", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("t", ctypes.c_int32), ("rank", ctypes.c_int32),
+                ("scale", ctypes.c_float)]
+
+
+@dataclass
+class AttnDesc:
+    """One rank of a ring of t: s_local query tokens, K/V blocks of s_local
+    tokens each; [tokens, b, heads, d] layouts."""
+    s_local: int
+    b: int
+    heads: int
+    d: int
+    t: int = 1
+    rank: int = 0
+    scale: float = 0.0          # 0: 1/sqrt(d)
+
+    def c(self):
+        sc = self.scale if self.scale > 0 else 1.0 / np.sqrt(self.d)
+        return spo_attn_desc(self.s_local, self.b, self.heads, self.d, self.t, self.rank, sc)
+
+
+def attention(d, q, k, v, L=None):
+    """Ordinary attention of the rank's queries over the keys of all t
+    blocks, float64.  q: s_local*b*heads*d bf16 bits; k, v: t times that.
+    Returns (o float64 [s_local*b*heads*d], lse float64 [s_local*b*heads])."""
+    L = L or lib()
+    n = d.s_local * d.b * d.heads * d.d
+    q = _check(q, np.uint16, n, "q")
+    k = _check(k, np.uint16, d.t * n, "k")
+    v = _check(v, np.uint16, d.t * n, "v")
+    o = np.empty(n, np.float64)
+    lse = np.empty(d.s_local * d.b * d.heads, np.float64)
+    if L.spo_attention(ctypes.byref(d.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse)) != 0:
+        raise ValueError("spo_attention rejected its arguments")
+    return o, lse
 
 
 # ---------------------------------------------------------------- region

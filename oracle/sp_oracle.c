@@ -482,3 +482,45 @@ void spo_layer_activation_elems(double s, double b, double h, double a, double t
     *tp = sbh * (10.0 + 24.0 / t + 5.0 * a * s / (h * t));
     *tp_sp = sbh / t * (34.0 + 5.0 * a * s / h);
 }
+
+/* ------------------------------------------------------------------------ */
+/* Ring attention: ordinary attention over all keys (see the header)         */
+/* ------------------------------------------------------------------------ */
+int spo_attention(const spo_attn_desc* d, const uint16_t* q, const uint16_t* k,
+                  const uint16_t* v, double* o_out, double* lse_out)
+{
+    if (!d || !q || !k || !v || !o_out || !lse_out) return -1;
+    if (d->s_local < 1 || d->b < 1 || d->heads < 1 || d->d < 1 || d->t < 1) return -1;
+    if (d->rank < 0 || d->rank >= d->t || !(d->scale > 0.0f)) return -1;
+    const int64_t S = d->s_local, B = d->b, NH = d->heads, D = d->d;
+    const int64_t nkeys = (int64_t)d->t * S;               /* keys per (batch, head) */
+    double* s = (double*)malloc((size_t)nkeys * sizeof(double));
+    if (!s) return -1;
+    /* element (token, batch, head, dim) of a [tokens][b][heads][d] tensor */
+#define AT(tok, bi, hh, dd) ((((tok) * B + (bi)) * NH + (hh)) * D + (dd))
+    for (int64_t qi = 0; qi < S; ++qi)
+        for (int64_t bi = 0; bi < B; ++bi)
+            for (int64_t hh = 0; hh < NH; ++hh) {
+                double m = -INFINITY;
+                for (int64_t j = 0; j < nkeys; ++j) {           /* key token j of the sequence */
+                    double dot = 0.0;
+                    for (int64_t dd = 0; dd < D; ++dd)
+                        dot += (double)spo_bf16_to_f32(q[AT(qi, bi, hh, dd)]) *
+                               (double)spo_bf16_to_f32(k[AT(j, bi, hh, dd)]);
+                    s[j] = (double)d->scale * dot;
+                    if (s[j] > m) m = s[j];
+                }
+                double l = 0.0;
+                for (int64_t j = 0; j < nkeys; ++j) l += exp(s[j] - m);
+                for (int64_t dd = 0; dd < D; ++dd) {
+                    double acc = 0.0;
+                    for (int64_t j = 0; j < nkeys; ++j)
+                        acc += exp(s[j] - m) * (double)spo_bf16_to_f32(v[AT(j, bi, hh, dd)]);
+                    o_out[AT(qi, bi, hh, dd)] = acc / l;
+                }
+                lse_out[(qi * B + bi) * NH + hh] = m + log(l);
+            }
+#undef AT
+    free(s);
+    return 0;
+}

@@ -151,6 +151,43 @@ int spo_activation_bytes(const spo_desc* d, uint64_t* saved_for_bwd,
 void spo_layer_activation_elems(double s, double b, double h, double a, double t,
                                 double* full, double* tp, double* tp_sp);
 
+/* ------------------------------------------------------------------------
+ * Ring attention (context parallelism), one rank's forward.
+ *
+ * Context parallelism shards Q, K and V along the sequence: rank i owns a
+ * contiguous block of query tokens and the matching K/V block.  Ring
+ * attention passes the K/V blocks around the ring; at each step a rank
+ * attends its queries to the block in hand and accumulates the partial
+ * online-softmax result, and after t steps every query has attended every
+ * key ("Sequence parallel math", section "Context parallelism and ring
+ * attention").  The pages apply no causal mask: every query sees every key.
+ * Whatever the order of the steps, the result is ordinary attention of the
+ * rank's queries over the whole sequence, which is what this function
+ * computes, in float64, straight from the definition:
+ *   s_j = scale * (q . k_j),  o = sum_j exp(s_j - m) v_j / sum_j exp(s_j - m),
+ *   lse = m + log(sum_j exp(s_j - m)),  m = max_j s_j,
+ * over the keys j of all t blocks with the query's batch index and head.
+ * Layouts (bf16 as raw 16-bit words): q [s_local][b][heads][d]; k and v
+ * [t][s_local][b][heads][d] (block j = the tokens of rank j); o_out
+ * [s_local][b][heads][d] and lse_out [s_local][b][heads] in float64.  rank
+ * does not change the result (it orders the ring).  Returns 0, or -1 on an
+ * invalid argument.
+ * Parity: pinned (torch float64 scaled_dot_product_attention, a single key,
+ * identical keys, constant values, a two-key closed form, invariance to the
+ * order of the key blocks). */
+typedef struct {
+    int64_t s_local;   /* query tokens of this rank = key tokens per block */
+    int64_t b;         /* batch                                            */
+    int32_t heads;     /* attention heads                                  */
+    int32_t d;         /* head dimension                                   */
+    int32_t t;         /* ring size (context-parallel degree)              */
+    int32_t rank;      /* this rank (owns query block `rank`)              */
+    float   scale;     /* softmax scale, usually 1/sqrt(d)                 */
+} spo_attn_desc;
+
+int spo_attention(const spo_attn_desc* d, const uint16_t* q, const uint16_t* k,
+                  const uint16_t* v, double* o_out, double* lse_out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -18,6 +18,8 @@ Recipe (the pages measure on no dataset; activations are synthetic by nature):
   generator, default_rng(seed + 1), draws nparts slabs of standard normals
   in rank order, each scaled by 1/sqrt(nparts) so that their sum has the
   unit variance of x.
+  Ring attention (make_attn_inputs): default_rng(seed + 2) draws q, then k
+  and v of all t blocks, standard normals rounded to bf16.
 """
 from dataclasses import dataclass, field
 
@@ -61,6 +63,18 @@ def make_parts(rows, h, io, nparts, seed=0):
     scale = np.float32(1.0 / np.sqrt(nparts))
     parts = rng.standard_normal((nparts, rows * h), dtype=np.float32) * scale
     return to_bf16_bits(parts) if io == BF16 else parts
+
+
+def make_attn_inputs(s_local, b, heads, d, t, seed=0):
+    """Ring attention: this rank's queries q [s_local*b*heads*d] and the
+    keys/values of all t blocks k, v [t*s_local*b*heads*d], standard normals
+    from default_rng(seed + 2) drawn in the order q, k, v, as bf16 bits."""
+    rng = np.random.default_rng(seed + 2)
+    n = s_local * b * heads * d
+    q = rng.standard_normal(n, dtype=np.float32)
+    k = rng.standard_normal(t * n, dtype=np.float32)
+    v = rng.standard_normal(t * n, dtype=np.float32)
+    return {"q": to_bf16_bits(q), "k": to_bf16_bits(k), "v": to_bf16_bits(v)}
 
 
 @dataclass

@@ -68,6 +68,13 @@ MUTANTS = {
                         "float hf = load_io(d->io, residual, i) + 0.0f;\n                hrow[c]"),
     "exit_dres_scaled": ("if (dres_out) store_io(d->io, dres_out, i, (float)dhv);",
                          "if (dres_out) store_io(d->io, dres_out, i, (float)(dy ? dhv : dxu));"),
+    # ring attention
+    "attn_scale_squared": ("s[j] = (double)d->scale * dot;", "s[j] = (double)d->scale * (double)d->scale * dot;"),
+    "attn_unnormalised": ("o_out[AT(qi, bi, hh, dd)] = acc / l;", "o_out[AT(qi, bi, hh, dd)] = acc;"),
+    "attn_lse_without_max": ("lse_out[(qi * B + bi) * NH + hh] = m + log(l);",
+                             "lse_out[(qi * B + bi) * NH + hh] = log(l);"),
+    "attn_keys_ignore_head": ("(double)spo_bf16_to_f32(k[AT(j, bi, hh, dd)]);",
+                              "(double)spo_bf16_to_f32(k[AT(j, bi, 0, dd)]);"),
     # reduce-scatter prologue
     "reduce_reversed_order": ("float acc = load_io(d->io, parts, i);                       /* rank 0 */\n"
                               "        for (int p = 1; p < nparts; ++p)",
@@ -88,7 +95,10 @@ def _checks(L, philox):
     from tests import test_oracle_accounting as A
     from tests import test_oracle_rs as S
     from tests import test_oracle_variants as V
+    from tests import test_oracle_attention as T
     c = [
+        lambda: T.test_matches_torch_sdpa_float64(L, 5, 2, 3, 16, 3, 1),
+        lambda: T.test_two_keys_closed_form(L),
         lambda: V.test_entry_h_is_the_residual_bit_for_bit(L, F32),
         lambda: V.test_entry_backward_matches_torch_autograd(L, LN),
         lambda: V.test_exit_backward_matches_torch_autograd(L, 0.3),
