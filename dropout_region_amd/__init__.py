@@ -56,6 +56,32 @@ class Desc:
                         self.norm, self.p, self.eps, self.seed, self.offset)
 
 
+class spr_attn_desc(ctypes.Structure):
+    _fields_ = [("s_local", ctypes.c_int64), ("b", ctypes.c_int64), ("heads", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("t", ctypes.c_int32), ("rank", ctypes.c_int32),
+                ("scale", ctypes.c_float)]
+
+
+@dataclass
+class AttnDesc:
+    """Ring attention on rank `rank` of t (include/sp_ring_attn.h)."""
+    s_local: int
+    b: int
+    heads: int
+    d: int
+    t: int = 1
+    rank: int = 0
+    scale: float = 0.0
+
+    @property
+    def rows(self):
+        return self.s_local * self.b * self.heads
+
+    def c(self):
+        return spr_attn_desc(self.s_local, self.b, self.heads, self.d, self.t, self.rank,
+                             self.scale)
+
+
 _lib = None
 
 
@@ -84,6 +110,15 @@ def lib():
         L.sp_region_bwd_workspace_bytes.restype = ctypes.c_size_t
         L.sp_region_activation_bytes.argtypes = [D, P, P]
         L.sp_region_activation_bytes.restype = ctypes.c_int
+        A = ctypes.POINTER(spr_attn_desc)
+        L.sp_ring_attn_workspace_bytes.argtypes = [A]
+        L.sp_ring_attn_workspace_bytes.restype = ctypes.c_size_t
+        L.sp_ring_attn_fwd.argtypes = [A, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.sp_ring_attn_fwd.restype = ctypes.c_int
+        L.sp_ring_attn_step.argtypes = [A, ctypes.c_int32, P, P, P, P, ctypes.c_size_t, P]
+        L.sp_ring_attn_step.restype = ctypes.c_int
+        L.sp_ring_attn_merge.argtypes = [A, P, P, P, ctypes.c_size_t, P]
+        L.sp_ring_attn_merge.restype = ctypes.c_int
         L.sp_region_status_string.argtypes = [ctypes.c_int]
         L.sp_region_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -231,6 +266,63 @@ def sp_region_bwd_launch(d, index, dy, dh_out, h, mask, mean, rstd, gamma, dx_ou
     st = lib().sp_region_bwd_launch(ctypes.byref(d.c()), int(index), *args, _stream(stream))
     if st != SPR_OK:
         raise SprError("sp_region_bwd_launch", st)
+
+
+# ------------------------------------------------------------ ring attention
+def sp_ring_attn_workspace_bytes(d):
+    return int(lib().sp_ring_attn_workspace_bytes(ctypes.byref(d.c())))
+
+
+def _ws(workspace):
+    if workspace is None or not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    return ctypes.c_void_p(workspace.data_ptr()), ctypes.c_size_t(
+        workspace.numel() * workspace.element_size())
+
+
+def sp_ring_attn_fwd(d, q, k, v, o_out, lse_out, workspace, stream=None):
+    import torch
+    n, dev = d.rows * d.d, q.device if q is not None else None
+    bf = torch.bfloat16
+    st = lib().sp_ring_attn_fwd(ctypes.byref(d.c()), _arg(q, "q", n, bf, dev),
+                                _arg(k, "k", d.t * n, bf, dev), _arg(v, "v", d.t * n, bf, dev),
+                                _arg(o_out, "o_out", n, bf, dev),
+                                _arg(lse_out, "lse_out", d.rows, torch.float32, dev, True),
+                                *_ws(workspace), _stream(stream))
+    if st != SPR_OK:
+        raise SprError("sp_ring_attn_fwd", st)
+
+
+def sp_ring_attn_step(d, step, q, k_blk, v_blk, workspace, stream=None):
+    import torch
+    n, dev = d.rows * d.d, q.device if q is not None else None
+    bf = torch.bfloat16
+    st = lib().sp_ring_attn_step(ctypes.byref(d.c()), ctypes.c_int32(int(step)),
+                                 _arg(q, "q", n, bf, dev), _arg(k_blk, "k_blk", n, bf, dev),
+                                 _arg(v_blk, "v_blk", n, bf, dev), *_ws(workspace),
+                                 _stream(stream))
+    if st != SPR_OK:
+        raise SprError("sp_ring_attn_step", st)
+
+
+def sp_ring_attn_merge(d, o_out, lse_out, workspace, stream=None):
+    import torch
+    n, dev = d.rows * d.d, o_out.device if o_out is not None else None
+    st = lib().sp_ring_attn_merge(ctypes.byref(d.c()), _arg(o_out, "o_out", n, torch.bfloat16, dev),
+                                  _arg(lse_out, "lse_out", d.rows, torch.float32, dev, True),
+                                  *_ws(workspace), _stream(stream))
+    if st != SPR_OK:
+        raise SprError("sp_ring_attn_merge", st)
+
+
+def ring_attn(d, q, k, v, stream=None):
+    """Allocates O, lse and the workspace; runs sp_ring_attn_fwd."""
+    import torch
+    o = torch.empty(d.rows * d.d, dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty(d.rows, dtype=torch.float32, device=q.device)
+    ws = torch.empty(max(sp_ring_attn_workspace_bytes(d), 256), dtype=torch.uint8, device=q.device)
+    sp_ring_attn_fwd(d, q, k, v, o, lse, ws, stream)
+    return o, lse
 
 
 # ------------------------------------------------------------ allocation helpers

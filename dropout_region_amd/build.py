@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsp_region.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["sp_fwd.hip", "sp_bwd.hip", "sp_region_api.hip"]
+SOURCES = ["sp_fwd.hip", "sp_bwd.hip", "sp_region_api.hip", "ring_attn.hip"]
 ARCH = "gfx950"
 
 

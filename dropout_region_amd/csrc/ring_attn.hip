@@ -1,0 +1,384 @@
+// ring_attn.hip -- one rank's ring-attention forward on gfx950 (context
+// parallelism).
+//
+// Context parallelism gives rank i a contiguous block of query tokens and the
+// matching K/V block; ring attention passes the K/V blocks around the ring
+// and, at each step, attends the rank's queries to the block in hand and
+// accumulates the partial online-softmax result, so that after t steps every
+// query has attended every key and no device holds more than an s/t x s/t
+// tile of scores ("Sequence parallel math", section "Context parallelism and
+// ring attention").  No causal mask: every query sees every key.
+//
+// Kernel 1 (step): one workgroup per (128-query tile, batch x head, ring
+// step); at step k the block in hand is block (rank - k) mod t.  It walks
+// that block's keys in tiles of 64 with an online softmax and writes the
+// step's partial result: O_k normalised by its own sum, and its
+// log-sum-exp.  Kernel 2 (merge): per query and head, folds the partials in
+// ring order, acc = merge(acc, partial_k) for k = 0 .. t-1 -- the
+// accumulation a ring performs as the blocks arrive.
+//
+// Matrix products on MFMA (v_mfma_f32_32x32x16_bf16; bf16 operands, fp32
+// accumulation).  Each wave owns 32 queries and computes S^T = K Q^T, so a
+// lane holds the scores of ONE query (lane mod 32) for 32 of a tile's 64
+// keys; the row max and sum need one exchange between the two half-waves.
+// P (bf16) then feeds O^T += V^T P^T straight from registers, with the keys
+// of each product taken in the order the score layout left them in (the
+// same order for V^T, read from a transposed V tile in LDS), and O^T keeps
+// one query per lane too, so the softmax rescale is one scalar per lane.
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include "sp_device.h"
+#include "sp_host_checks.h"
+#include "sp_ring_attn.h"
+
+namespace spr {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+struct AttnArgs {
+    const __bf16* q;       // [s_local][b][heads][d]
+    const __bf16* k;       // fused: [t][s_local][b][heads][d]; one step: the block in hand
+    const __bf16* v;
+    float* part_o;         // [t][s_local][b][heads][d] fp32, normalised per step
+    float* part_lse;       // [t][s_local][b][heads] fp32 (natural log)
+    __bf16* o_out;         // [s_local][b][heads][d]
+    float* lse_out;        // [s_local][b][heads]
+    int64_t s_local, b;
+    int heads, t, rank;
+    int step0;             // ring step of blockIdx.z == 0
+    int fused;             // 1: k/v hold all t blocks, block (rank - step) mod t is used
+    float scale_log2;      // softmax scale * log2(e): scores in base-2 units
+};
+
+constexpr int kQT = 128;   // queries per workgroup (4 waves x 32)
+constexpr int kKT = 64;    // keys per tile
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int D>
+__global__ void __launch_bounds__(256) ring_attn_step_kernel(AttnArgs a) {
+    constexpr int KS = D / 16;          // k-steps of S^T = K Q^T
+    constexpr int DB = D / 32;          // 32-row blocks of O^T
+    constexpr int KP = D + 8;           // K tile pitch (elements)
+    constexpr int VP = kKT + 8;         // transposed V tile pitch
+    constexpr int CH = kKT * D / 8;     // 16-byte chunks per K (or V) tile
+    constexpr int CPT = CH / 256;       // chunks per thread
+    static_assert(CH % 256 == 0, "tile chunks must split evenly over the workgroup");
+    __shared__ __attribute__((aligned(16))) __bf16 ks[kKT * KP];   // K tile [key][d]
+    __shared__ __attribute__((aligned(16))) __bf16 vt[D * VP];     // V tile [d][key]
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 5, c = lane & 31;
+    const int bi = (int)(blockIdx.y / a.heads), hh = (int)(blockIdx.y % a.heads);
+    const int step = a.step0 + (int)blockIdx.z;
+    const int blk = a.fused ? (a.rank - step % a.t + a.t) % a.t : 0;
+    const int64_t tok = a.b * a.heads * D;                     // elements per token
+    const int64_t head_off = ((int64_t)bi * a.heads + hh) * D;
+    const int64_t qrow = (int64_t)blockIdx.x * kQT + wave * 32 + c;
+    const int64_t qr = qrow < a.s_local ? qrow : a.s_local - 1;
+
+    // Q^T operand: lane holds query c, d = 16*s + 8*g + 0..7.
+    bf16x8 qv[KS];
+    const __bf16* qp = a.q + qr * tok + head_off;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        const uint4 w = load_stream(qp + 16 * s + 8 * g);
+        qv[s] = __builtin_bit_cast(bf16x8, w);
+    }
+
+    const __bf16* kb = a.k + (int64_t)blk * a.s_local * tok + head_off;
+    const __bf16* vb = a.v + (int64_t)blk * a.s_local * tok + head_off;
+
+    // The next tile's K and V chunks travel in registers while this tile is
+    // computed.  Chunk cc = tid + 256*i: key cc / (D/8), d = 8 * (cc % (D/8)).
+    uint4 kn[CPT], vn[CPT];
+    auto fetch = [&](int64_t k0) {
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int cc = tid + 256 * i, key = cc / (D / 8), dc = cc % (D / 8);
+            const int64_t kk = k0 + key < a.s_local ? k0 + key : a.s_local - 1;   // clamp
+            kn[i] = load_stream(kb + kk * tok + 8 * dc);
+            vn[i] = load_stream(vb + kk * tok + 8 * dc);
+        }
+    };
+    auto stage = [&]() {
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int cc = tid + 256 * i, key = cc / (D / 8), dc = cc % (D / 8);
+            *reinterpret_cast<uint4*>(&ks[key * KP + 8 * dc]) = kn[i];
+            const bf16x8 v8 = __builtin_bit_cast(bf16x8, vn[i]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vt[(8 * dc + e) * VP + key] = v8[e];
+        }
+    };
+
+    f32x16 o[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
+    float m = -INFINITY, l = 0.0f;      // running max (base-2 units) and sum of this query
+
+    fetch(0);
+    for (int64_t k0 = 0; k0 < a.s_local; k0 += kKT) {
+        __syncthreads();                // every wave is done with the previous tile
+        stage();
+        __syncthreads();
+        if (k0 + kKT < a.s_local) fetch(k0 + kKT);
+
+        // S^T = K Q^T for keys 32*cb .. 32*cb+31 of the tile.
+        f32x16 st[2];
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) st[cb][r] = 0.0f;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&ks[(32 * cb + c) * KP + 16 * s + 8 * g]);
+                st[cb] = mfma32(ka, qv[s], st[cb]);
+            }
+        }
+        // Register r of block cb holds key 32*cb + 8*(r/4) + 4*g + r%4.
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t key = k0 + 32 * cb + 8 * (r / 4) + 4 * g + (r % 4);
+                const float x = key < a.s_local ? st[cb][r] * a.scale_log2 : -INFINITY;
+                st[cb][r] = x;
+                tmax = fmaxf(tmax, x);
+            }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        const float m_new = fmaxf(m, tmax);        // finite: every tile has a key
+        const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+        float psum = 0.0f;
+        bf16x8 pb[4];                               // P^T operands, keys as above
+#pragma unroll
+        for (int kg = 0; kg < 4; ++kg)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float p = __builtin_amdgcn_exp2f(st[kg >> 1][8 * (kg & 1) + e] - m_new);
+                psum += p;
+                pb[kg][e] = (__bf16)p;
+            }
+        psum += __shfl_xor(psum, 32);
+        l = l * alpha + psum;
+        m = m_new;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+
+        // O^T += V^T P^T.  Product kg covers keys 32*(kg/2) + 16*(kg%2) + {4g..4g+3,
+        // 8+4g..8+4g+3} for lane group g: the keys its P^T operand holds.
+#pragma unroll
+        for (int kg = 0; kg < 4; ++kg) {
+            const int kbase = 32 * (kg >> 1) + 16 * (kg & 1) + 4 * g;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const __bf16* vr = &vt[(32 * db + c) * VP + kbase];
+                const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vr);
+                const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vr + 8);
+                const bf16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                o[db] = mfma32(va, pb[kg], o[db]);
+            }
+        }
+    }
+
+    // The step's partial: O / l and its log-sum-exp (natural log).
+    if (qrow < a.s_local) {
+        const int64_t row = ((int64_t)step * a.s_local + qrow) * a.b * a.heads +
+                            (int64_t)bi * a.heads + hh;
+        const float inv_l = 1.0f / l;
+        float* po = a.part_o + row * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4)   // d = 32*db + 8*q4 + 4*g + 0..3
+                *reinterpret_cast<float4*>(po + 32 * db + 8 * q4 + 4 * g) =
+                    make_float4(o[db][4 * q4] * inv_l, o[db][4 * q4 + 1] * inv_l,
+                                o[db][4 * q4 + 2] * inv_l, o[db][4 * q4 + 3] * inv_l);
+        if (g == 0) a.part_lse[row] = (m + __log2f(l)) * 0.69314718055994531f;
+    }
+}
+
+// Merge: per (query, batch, head) row, the t partials in ring order.  A row
+// is D/4 threads, each owning 4 consecutive d; the folded result is written
+// as bf16 O and fp32 log-sum-exp.
+template <int D>
+__global__ void __launch_bounds__(256) ring_attn_merge_kernel(AttnArgs a) {
+    constexpr int TPR = D / 4;
+    const int64_t nrows = a.s_local * a.b * a.heads;
+    const int64_t row = (int64_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
+    const int d0 = 4 * (threadIdx.x % TPR);
+    if (row >= nrows) return;
+    float lse = a.part_lse[row];
+    float4 o = *reinterpret_cast<const float4*>(a.part_o + row * D + d0);
+    for (int k = 1; k < a.t; ++k) {
+        const int64_t pr = (int64_t)k * nrows + row;
+        const float lk = a.part_lse[pr];
+        const float4 ok = *reinterpret_cast<const float4*>(a.part_o + pr * D + d0);
+        const float mx = fmaxf(lse, lk);
+        const float wa = __expf(lse - mx), wb = __expf(lk - mx);
+        const float inv = 1.0f / (wa + wb);
+        o.x = (o.x * wa + ok.x * wb) * inv;
+        o.y = (o.y * wa + ok.y * wb) * inv;
+        o.z = (o.z * wa + ok.z * wb) * inv;
+        o.w = (o.w * wa + ok.w * wb) * inv;
+        lse = mx + __logf(wa + wb);
+    }
+    const uint32_t lo = pack_bf16x2(o.x, o.y), hi = pack_bf16x2(o.z, o.w);
+    *reinterpret_cast<uint2*>(a.o_out + row * D + d0) = make_uint2(lo, hi);
+    if (d0 == 0 && a.lse_out) a.lse_out[row] = lse;
+}
+
+template <int D>
+static hipError_t launch_attn(const AttnArgs& a, int steps, bool merge, hipStream_t s) {
+    const dim3 g((unsigned)((a.s_local + kQT - 1) / kQT), (unsigned)(a.b * a.heads),
+                 (unsigned)steps);
+    hipLaunchKernelGGL(ring_attn_step_kernel<D>, g, dim3(256), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !merge) return e;
+    const int64_t nrows = a.s_local * a.b * a.heads;
+    const int64_t rpb = 256 / (D / 4);
+    hipLaunchKernelGGL(ring_attn_merge_kernel<D>, dim3((unsigned)((nrows + rpb - 1) / rpb)),
+                       dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_ring_attn(int d, const AttnArgs& a, int steps, bool merge, hipStream_t s) {
+    switch (d) {
+        case 64: return launch_attn<64>(a, steps, merge, s);
+        case 128: return launch_attn<128>(a, steps, merge, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace spr
+
+using namespace spr;
+
+namespace {
+
+bool attn_desc_ok(const spr_attn_desc* d) {
+    if (!d) return false;
+    if (d->s_local < 1 || d->b < 1 || d->heads < 1 || d->t < 1 || d->t > 65535) return false;
+    if (d->rank < 0 || d->rank >= d->t) return false;
+    if (d->d != 64 && d->d != 128) return false;
+    if (d->b * (int64_t)d->heads > 65535) return false;
+    if (!(d->scale >= 0.0f) || isinf(d->scale)) return false;               // also NaN
+    // every index (t blocks of s_local*b*heads*d elements) well inside 63 bits
+    if ((double)d->t * (double)d->s_local * (double)d->b * d->heads * d->d > 4.0e18) return false;
+    return true;
+}
+
+uint64_t rows_of(const spr_attn_desc* d) { return (uint64_t)d->s_local * d->b * d->heads; }
+
+// Workspace: part_o (t*rows*d fp32), then part_lse (t*rows fp32), 256-aligned.
+uint64_t part_o_bytes(const spr_attn_desc* d) {
+    return ((uint64_t)d->t * rows_of(d) * d->d * 4u + 255u) & ~(uint64_t)255u;
+}
+uint64_t workspace_need(const spr_attn_desc* d) {
+    return part_o_bytes(d) + (((uint64_t)d->t * rows_of(d) * 4u + 255u) & ~(uint64_t)255u);
+}
+
+AttnArgs make_args(const spr_attn_desc* d, void* workspace) {
+    AttnArgs a{};
+    a.part_o = static_cast<float*>(workspace);
+    a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + part_o_bytes(d));
+    a.s_local = d->s_local;
+    a.b = d->b;
+    a.heads = d->heads;
+    a.t = d->t;
+    a.rank = d->rank;
+    const double scale = d->scale > 0.0f ? (double)d->scale : 1.0 / sqrt((double)d->d);
+    a.scale_log2 = (float)((double)(float)scale * 1.4426950408889634);
+    return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sp_ring_attn_workspace_bytes(const spr_attn_desc* d) {
+    return attn_desc_ok(d) ? (size_t)workspace_need(d) : 0;
+}
+
+spr_status sp_ring_attn_step(const spr_attn_desc* d, int32_t step, const void* q,
+                             const void* k_blk, const void* v_blk, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+    if (!attn_desc_ok(d)) return SPR_ERR_INVALID_ARG;
+    if (step < 0 || step >= d->t || !q || !k_blk || !v_blk) return SPR_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k_blk, 16) || !aligned(v_blk, 16)) return SPR_ERR_INVALID_ARG;
+    const uint64_t need = workspace_need(d);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return SPR_ERR_WORKSPACE;
+    const uint64_t blk = rows_of(d) * d->d * 2u;
+    const Range outs[] = {range_of(workspace, need)};
+    const Range ins[] = {range_of(q, blk), range_of(k_blk, blk), range_of(v_blk, blk)};
+    if (!disjoint(outs, 1, ins, 3)) return SPR_ERR_INVALID_ARG;
+    AttnArgs a = make_args(d, workspace);
+    a.q = static_cast<const __bf16*>(q);
+    a.k = static_cast<const __bf16*>(k_blk);
+    a.v = static_cast<const __bf16*>(v_blk);
+    a.step0 = step;
+    a.fused = 0;
+    return launch_ring_attn(d->d, a, 1, false, stream) == hipSuccess ? SPR_OK : SPR_ERR_HIP;
+}
+
+spr_status sp_ring_attn_merge(const spr_attn_desc* d, void* o_out, float* lse_out,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!attn_desc_ok(d) || !o_out) return SPR_ERR_INVALID_ARG;
+    if (!aligned(o_out, 16) || !aligned(lse_out, 4)) return SPR_ERR_INVALID_ARG;
+    const uint64_t need = workspace_need(d);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return SPR_ERR_WORKSPACE;
+    const Range outs[] = {range_of(o_out, rows_of(d) * d->d * 2u),
+                          range_of(lse_out, rows_of(d) * 4u)};
+    const Range ins[] = {range_of(workspace, need)};
+    if (!disjoint(outs, 2, ins, 1)) return SPR_ERR_INVALID_ARG;
+    AttnArgs a = make_args(d, workspace);
+    a.o_out = static_cast<__bf16*>(o_out);
+    a.lse_out = lse_out;
+    const int64_t nrows = (int64_t)rows_of(d);
+    const int64_t rpb = 256 / (d->d / 4);
+    if (d->d == 64)
+        hipLaunchKernelGGL(ring_attn_merge_kernel<64>, dim3((unsigned)((nrows + rpb - 1) / rpb)),
+                           dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL(ring_attn_merge_kernel<128>, dim3((unsigned)((nrows + rpb - 1) / rpb)),
+                           dim3(256), 0, stream, a);
+    return hipGetLastError() == hipSuccess ? SPR_OK : SPR_ERR_HIP;
+}
+
+spr_status sp_ring_attn_fwd(const spr_attn_desc* d, const void* q, const void* k,
+                            const void* v, void* o_out, float* lse_out, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+    if (!attn_desc_ok(d)) return SPR_ERR_INVALID_ARG;
+    if (!q || !k || !v || !o_out) return SPR_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o_out, 16) ||
+        !aligned(lse_out, 4))
+        return SPR_ERR_INVALID_ARG;
+    const uint64_t need = workspace_need(d);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return SPR_ERR_WORKSPACE;
+    const uint64_t blk = rows_of(d) * d->d * 2u;
+    const Range outs[] = {range_of(o_out, blk), range_of(lse_out, rows_of(d) * 4u),
+                          range_of(workspace, need)};
+    const Range ins[] = {range_of(q, blk), range_of(k, blk * d->t), range_of(v, blk * d->t)};
+    if (!disjoint(outs, 3, ins, 3)) return SPR_ERR_INVALID_ARG;
+    AttnArgs a = make_args(d, workspace);
+    a.q = static_cast<const __bf16*>(q);
+    a.k = static_cast<const __bf16*>(k);
+    a.v = static_cast<const __bf16*>(v);
+    a.o_out = static_cast<__bf16*>(o_out);
+    a.lse_out = lse_out;
+    a.step0 = 0;
+    a.fused = 1;
+    return launch_ring_attn(d->d, a, d->t, true, stream) == hipSuccess ? SPR_OK : SPR_ERR_HIP;
+}
+
+}  // extern "C"

@@ -11,7 +11,8 @@ import dropout_region_amd as spr
 import oracle
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "sp_region.h")
+HEADERS = [os.path.join(ROOT, "include", "sp_region.h"),
+           os.path.join(ROOT, "include", "sp_ring_attn.h")]
 
 
 @pytest.fixture(scope="module")
@@ -22,9 +23,9 @@ def L():
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(sp_region_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(sp_(?:region|ring_attn)_\w+)\s*\(", text)))
 
 
 def test_header_declares_the_boundary():
@@ -33,7 +34,9 @@ def test_header_declares_the_boundary():
                             "sp_region_bwd_exit",
                             "sp_region_bwd_workspace_bytes",
                             "sp_region_bwd_num_launches", "sp_region_bwd_launch",
-                            "sp_region_activation_bytes", "sp_region_status_string"])
+                            "sp_region_activation_bytes", "sp_region_status_string",
+                            "sp_ring_attn_workspace_bytes", "sp_ring_attn_fwd",
+                            "sp_ring_attn_step", "sp_ring_attn_merge"])
 
 
 def test_library_exports_every_declared_function(L):
@@ -193,3 +196,31 @@ def test_activation_bytes_agree_with_oracle(L, olib, io, norm, p):
         d = spr.Desc(s_local=s_local, b=b, h=h, io=io, norm=norm, p=p)
         od = oracle.Desc(s_local=s_local, b=b, h=h, io=io, norm=norm, p=p)
         assert spr.sp_region_activation_bytes(d) == oracle.activation_bytes(od, L=olib)
+
+
+def test_ring_attn_rejects_bad_calls(L):
+    def desc(**kw):
+        base = dict(s_local=128, b=1, heads=2, d=128, t=4, rank=1, scale=0.0)
+        base.update(kw)
+        return spr.AttnDesc(**base).c()
+    assert L.sp_ring_attn_workspace_bytes(ctypes.byref(desc())) > 0
+    for bad in (dict(d=96), dict(rank=4), dict(rank=-1), dict(t=0), dict(s_local=0),
+                dict(heads=70000), dict(scale=float("nan")), dict(scale=-1.0)):
+        d = desc(**bad)
+        assert L.sp_ring_attn_workspace_bytes(ctypes.byref(d)) == 0, bad
+        assert L.sp_ring_attn_fwd(ctypes.byref(d), *[ctypes.c_void_p(A + i * 0x1000000) for i in range(5)],
+                                  ctypes.c_void_p(A + 0x8000000), ctypes.c_size_t(1 << 30),
+                                  None) == spr.SPR_ERR_INVALID_ARG, bad
+    d = desc()
+    need = L.sp_ring_attn_workspace_bytes(ctypes.byref(d))
+    ptrs = [ctypes.c_void_p(A + i * 0x1000000) for i in range(5)]
+    assert L.sp_ring_attn_fwd(ctypes.byref(d), *ptrs, ctypes.c_void_p(A + 0x8000000),
+                              ctypes.c_size_t(need - 1), None) == spr.SPR_ERR_WORKSPACE
+    ptrs[3] = ctypes.c_void_p(A + 0x1000000)     # o_out aliases k
+    assert L.sp_ring_attn_fwd(ctypes.byref(d), *ptrs, ctypes.c_void_p(A + 0x8000000),
+                              ctypes.c_size_t(need), None) == spr.SPR_ERR_INVALID_ARG
+    for step in (-1, 4):
+        assert L.sp_ring_attn_step(ctypes.byref(d), step, *[ctypes.c_void_p(A + i * 0x1000000)
+                                                           for i in range(3)],
+                                   ctypes.c_void_p(A + 0x8000000), ctypes.c_size_t(need),
+                                   None) == spr.SPR_ERR_INVALID_ARG

@@ -1,0 +1,102 @@
+"""GPU parity of the ring-attention forward (include/sp_ring_attn.h) against
+the oracle's ordinary attention over all keys.
+
+Tolerance, from the arithmetic: the scores are exact bf16 products summed in
+fp32; the probabilities are rounded to bf16 before P V (relative error at
+most 2^-9 each), so O may move by at most 2^-9 * max|V| from that; the merge
+runs in fp32 and O is rounded to bf16 once.  Per element:
+  |O_gpu - O| <= ulp_bf16(O) + 2^-9 * max|V|,
+and, on average, well inside that (mean error <= 2^-12 * max|V|).
+lse (fp32): |lse_gpu - lse| <= 1e-4 + 1e-5 * |lse|."""
+import zlib
+
+import numpy as np
+import pytest
+
+import dropout_region_amd as spr
+import oracle
+from sp_inputs import make_attn_inputs
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    spr.lib()
+
+
+def _dev(bits):
+    return P.to_device(bits, P.BF16)
+
+
+def check_attention(name, got_o, got_lse, want_o, want_lse, v_bits):
+    vmax = float(np.max(np.abs(oracle.bf16_to_f32(v_bits))))
+    a = oracle.bf16_to_f32(got_o).astype(np.float64)
+    err = np.abs(a - want_o)
+    bound = P.ulp_bf16(want_o) + 2.0 ** -9 * vmax
+    bad = np.flatnonzero(err > bound)
+    assert bad.size == 0, (f"{name}: {bad.size} of {err.size} outside the bound; first at "
+                           f"{bad[0]}: {a[bad[0]]} vs {want_o[bad[0]]}")
+    assert err.mean() <= 2.0 ** -12 * vmax, f"{name}: mean error {err.mean()} too large"
+    if got_lse is not None:
+        lerr = np.abs(got_lse.astype(np.float64) - want_lse)
+        assert np.all(lerr <= 1e-4 + 1e-5 * np.abs(want_lse)), f"{name}: lse off by {lerr.max()}"
+
+
+CASES = {
+    "d128_full_tiles_t4_rank1": dict(s_local=256, b=1, heads=2, d=128, t=4, rank=1),
+    "d64_ragged_b2_t3_rank2": dict(s_local=100, b=2, heads=3, d=64, t=3, rank=2),
+    "d128_one_token_t1": dict(s_local=1, b=1, heads=1, d=128, t=1, rank=0),
+    "d64_two_tiles_ragged_t2": dict(s_local=130, b=1, heads=4, d=64, t=2, rank=0),
+    "d128_t8_rank7": dict(s_local=64, b=1, heads=2, d=128, t=8, rank=7),
+    "d128_given_scale": dict(s_local=70, b=2, heads=1, d=128, t=2, rank=1, scale=0.05),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_ring_attention_matches_oracle(name):
+    kw = CASES[name]
+    d, od = spr.AttnDesc(**kw), oracle.AttnDesc(**kw)
+    _say(f"[case] ring attention {name}: {kw}")
+    x = make_attn_inputs(d.s_local, d.b, d.heads, d.d, d.t, seed=zlib.crc32(name.encode()) % 1000)
+    want_o, want_lse = oracle.attention(od, x["q"], x["k"], x["v"])
+    o, lse = spr.ring_attn(d, _dev(x["q"]), _dev(x["k"]), _dev(x["v"]))
+    check_attention(name, P.to_host(o), P.to_host(lse), want_o, want_lse, x["v"])
+
+
+def test_steps_in_any_order_then_merge_equal_the_fused_call():
+    import torch
+    kw = dict(s_local=192, b=1, heads=3, d=128, t=4, rank=2)
+    d = spr.AttnDesc(**kw)
+    _say(f"[case] ring attention steps: {kw}")
+    x = make_attn_inputs(d.s_local, d.b, d.heads, d.d, d.t, seed=9)
+    q, k, v = _dev(x["q"]), _dev(x["k"]), _dev(x["v"])
+    o_f, lse_f = spr.ring_attn(d, q, k, v)
+    n = d.rows * d.d
+    ws = torch.zeros(spr.sp_ring_attn_workspace_bytes(d), dtype=torch.uint8, device=q.device)
+    for step in (3, 0, 2, 1):                      # any order: each step has its own slot
+        blk = (d.rank - step) % d.t
+        spr.sp_ring_attn_step(d, step, q, k[blk * n:(blk + 1) * n], v[blk * n:(blk + 1) * n], ws)
+    o = torch.empty_like(o_f)
+    spr.sp_ring_attn_merge(d, o, None, ws)        # lse may be omitted
+    torch.cuda.synchronize()
+    P.exact("o (steps + merge vs fused)", P.to_host(o), P.to_host(o_f))
+
+
+def test_rank_changes_only_the_order():
+    """Every rank of the ring sees the same keys in a different order: the
+    results agree within the tolerance (and each matches the oracle)."""
+    kw = dict(s_local=128, b=1, heads=2, d=64, t=4)
+    x = make_attn_inputs(kw["s_local"], 1, 2, 64, 4, seed=10)
+    want_o, want_lse = oracle.attention(oracle.AttnDesc(**kw), x["q"], x["k"], x["v"])
+    for rank in range(4):
+        d = spr.AttnDesc(rank=rank, **kw)
+        o, lse = spr.ring_attn(d, _dev(x["q"]), _dev(x["k"]), _dev(x["v"]))
+        check_attention(f"rank {rank}", P.to_host(o), P.to_host(lse), want_o, want_lse, x["v"])
