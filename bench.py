@@ -204,6 +204,112 @@ def load_traffic(workload):
     return t["kernels"] if t.get("source_hash") == kernel_source_hash() else None
 
 
+# ------------------------------------------------------------------ ring attention
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+ATTN_METRIC = "tokens/s and TFLOP/s (% of bf16 MFMA peak) for one rank's ring-attention forward, 1 GPU"
+
+
+def attn_cpu_baseline(w, min_seconds=10.0):
+    """The oracle (float64, one thread) on a bounded sample: query tokens
+    [0, n) of the rank against every key of every block, all heads, doubled
+    until it takes min_seconds.  Returns tokens/s scaled from the sample."""
+    import oracle
+    from oracle import build as obuild
+    from sp_inputs import make_attn_inputs
+    if not os.path.exists(oracle.LIB_PATH):
+        obuild.build_oracle()
+    od = oracle.AttnDesc(s_local=w.s_local, b=w.b, heads=w.heads, d=w.d, t=w.t)
+    x = make_attn_inputs(w.s_local, w.b, w.heads, w.d, w.t, seed=w.seed)
+    tok = w.b * w.heads * w.d
+    n = 1
+    while True:
+        t0 = time.perf_counter()
+        oracle.attention(od, x["q"][:n * tok], x["k"], x["v"], rows=(0, n))
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds or n >= w.s_local:
+            break
+        n = min(w.s_local, n * 2 if dt < min_seconds / 4 else n + max(1, int(n * (min_seconds / dt - 1))))
+    return {"value": round(n / dt, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} of {w.s_local} query tokens x all {w.s} keys x {w.b * w.heads} "
+                      f"(batch, head) pairs, float64 ({dt:.1f} s, 1 thread)"}
+
+
+def bench_attention(args, w):
+    import numpy as np
+    import torch
+    import dropout_region_amd as spr
+    from sp_inputs import make_attn_inputs
+    from tests import parity as P
+    dev = torch.device("cuda:0")
+    spr.lib()
+    d = spr.AttnDesc(s_local=w.s_local, b=w.b, heads=w.heads, d=w.d, t=w.t, rank=0)
+    print(f"[bench] ring attention {w.name}: {w.s_local} queries x {w.s} keys, {w.b}x{w.heads} "
+          f"heads of {w.d} on {torch.cuda.get_device_name(0)}", file=sys.stderr, flush=True)
+    x = make_attn_inputs(w.s_local, w.b, w.heads, w.d, w.t, seed=w.seed)
+    q, k, v = (P.to_device(x[n], P.BF16) for n in ("q", "k", "v"))
+    o = torch.empty(d.rows * d.d, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(d.rows, dtype=torch.float32, device=dev)
+    ws = torch.empty(spr.sp_ring_attn_workspace_bytes(d), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def fwd():
+        spr.sp_ring_attn_fwd(d, q, k, v, o, lse, ws, stream)
+
+    if not args.no_parity:                       # sampled query tokens against the oracle
+        import oracle
+        from tests.test_gpu_attention import check_attention
+        fwd()
+        torch.cuda.synchronize()
+        od = oracle.AttnDesc(s_local=w.s_local, b=w.b, heads=w.heads, d=w.d, t=w.t)
+        tok, go, gl = w.b * w.heads * w.d, P.to_host(o), P.to_host(lse)
+        for r in sorted({0, w.s_local // 2, w.s_local - 1}):
+            wo, wl = oracle.attention(od, x["q"][r * tok:(r + 1) * tok], x["k"], x["v"],
+                                      rows=(r, r + 1))
+            check_attention(f"query {r}", go[r * tok:(r + 1) * tok],
+                            gl[r * w.b * w.heads:(r + 1) * w.b * w.heads], wo, wl, x["v"])
+        print("[bench] parity ok on sampled queries", file=sys.stderr, flush=True)
+
+    for _ in range(args.warmup):
+        fwd()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        fwd()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    # the merge alone, on the same workspace: the step kernel is the rest
+    m0, m1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    m0.record(stream)
+    for _ in range(args.steps):
+        spr.sp_ring_attn_merge(d, o, lse, ws, stream)
+    m1.record(stream)
+    torch.cuda.synchronize()
+    merge_us = m0.elapsed_time(m1) / args.steps * 1e3
+    step_us = ms * 1e3 - merge_us
+    tflops = w.flops / (step_us * 1e-6) / 1e12
+    out = {
+        "metric": ATTN_METRIC, "value": round(w.s_local / (ms / 1e3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "s": w.s, "t": w.t, "rank": 0, "queries": w.s_local,
+                   "b": w.b, "heads": w.heads, "head_dim": w.d, "causal": False},
+        "tflops": round(w.flops / (ms * 1e-3) / 1e12, 1),
+        "kernels_us": {"ring_attn_step_kernel (t steps)": round(step_us, 2),
+                       "ring_attn_merge_kernel": round(merge_us, 2)},
+        "roofline": {"bound": "mfma", "kernel": "ring_attn_step_kernel", "achieved": round(tflops, 1),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "algorithmic_flops_per_launch": w.flops, "launch_us": round(step_us, 2)},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = attn_cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+
+
 # ------------------------------------------------------------------ bench
 def main():
     ap = argparse.ArgumentParser()
@@ -238,6 +344,10 @@ def main():
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
               "(the region is per-rank; there are no collectives to run)", file=sys.stderr)
         sys.exit(2)
+
+    from sp_inputs import ATTN_WORKLOADS
+    if wname in ATTN_WORKLOADS:
+        return bench_attention(args, ATTN_WORKLOADS[wname])
 
     import numpy as np
     import torch

@@ -36,6 +36,7 @@ namespace spr {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 struct AttnArgs {
@@ -61,7 +62,7 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 }
 
 template <int D>
-__global__ void __launch_bounds__(256) ring_attn_step_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(256, 2) ring_attn_step_kernel(AttnArgs a) {
     constexpr int KS = D / 16;          // k-steps of S^T = K Q^T
     constexpr int DB = D / 32;          // 32-row blocks of O^T
     constexpr int KP = D + 8;           // K tile pitch (elements)
@@ -94,8 +95,12 @@ __global__ void __launch_bounds__(256) ring_attn_step_kernel(AttnArgs a) {
     const __bf16* kb = a.k + (int64_t)blk * a.s_local * tok + head_off;
     const __bf16* vb = a.v + (int64_t)blk * a.s_local * tok + head_off;
 
-    // The next tile's K and V chunks travel in registers while this tile is
-    // computed.  Chunk cc = tid + 256*i: key cc / (D/8), d = 8 * (cc % (D/8)).
+    // The next tile's K and V travel in registers while this tile is
+    // computed.  K: chunk cc = tid + 256*i is key cc / (D/8), d = 8*(cc % (D/8)).
+    // V: a thread owns one 8-wide d chunk of R consecutive keys, so its
+    // transposed store is eight R-key runs (one 2R-byte write each).
+    constexpr int R = CPT >= 4 ? 4 : CPT;
+    static_assert(CPT % R == 0 && (R == 2 || R == 4), "V is staged in runs of 2 or 4 keys");
     uint4 kn[CPT], vn[CPT];
     auto fetch = [&](int64_t k0) {
 #pragma unroll
@@ -103,7 +108,11 @@ __global__ void __launch_bounds__(256) ring_attn_step_kernel(AttnArgs a) {
             const int cc = tid + 256 * i, key = cc / (D / 8), dc = cc % (D / 8);
             const int64_t kk = k0 + key < a.s_local ? k0 + key : a.s_local - 1;   // clamp
             kn[i] = load_stream(kb + kk * tok + 8 * dc);
-            vn[i] = load_stream(vb + kk * tok + 8 * dc);
+            // V: unit u = tid + 256*(i/R) -> d chunk u % (D/8), key group u / (D/8),
+            // key R*group + i%R
+            const int u = tid + 256 * (i / R), vdc = u % (D / 8), vkey = R * (u / (D / 8)) + (i % R);
+            const int64_t vk = k0 + vkey < a.s_local ? k0 + vkey : a.s_local - 1;
+            vn[i] = load_stream(vb + vk * tok + 8 * vdc);
         }
     };
     auto stage = [&]() {
@@ -111,9 +120,23 @@ __global__ void __launch_bounds__(256) ring_attn_step_kernel(AttnArgs a) {
         for (int i = 0; i < CPT; ++i) {
             const int cc = tid + 256 * i, key = cc / (D / 8), dc = cc % (D / 8);
             *reinterpret_cast<uint4*>(&ks[key * KP + 8 * dc]) = kn[i];
-            const bf16x8 v8 = __builtin_bit_cast(bf16x8, vn[i]);
+        }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) vt[(8 * dc + e) * VP + key] = v8[e];
+        for (int iu = 0; iu < CPT / R; ++iu) {
+            const int u = tid + 256 * iu, vdc = u % (D / 8), vkey = R * (u / (D / 8));
+            bf16x8 v8[R];
+#pragma unroll
+            for (int j = 0; j < R; ++j) v8[j] = __builtin_bit_cast(bf16x8, vn[R * iu + j]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                if constexpr (R == 4) {
+                    const bf16x4 run = {v8[0][e], v8[1][e], v8[2][e], v8[3][e]};
+                    *reinterpret_cast<bf16x4*>(&vt[(8 * vdc + e) * VP + vkey]) = run;
+                } else {
+                    const bf16x2 run = {v8[0][e], v8[1][e]};
+                    *reinterpret_cast<bf16x2*>(&vt[(8 * vdc + e) * VP + vkey]) = run;
+                }
+            }
         }
     };
 
@@ -143,37 +166,43 @@ __global__ void __launch_bounds__(256) ring_attn_step_kernel(AttnArgs a) {
                 st[cb] = mfma32(ka, qv[s], st[cb]);
             }
         }
-        // Register r of block cb holds key 32*cb + 8*(r/4) + 4*g + r%4.
+        // Register r of block cb holds key 32*cb + 8*(r/4) + 4*g + r%4.  The
+        // max is taken on the raw scores (the scale is positive) and the
+        // scale enters through the exponent's FMA: p = 2^(s*c - m).
         float tmax = -INFINITY;
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int64_t key = k0 + 32 * cb + 8 * (r / 4) + 4 * g + (r % 4);
-                const float x = key < a.s_local ? st[cb][r] * a.scale_log2 : -INFINITY;
-                st[cb][r] = x;
-                tmax = fmaxf(tmax, x);
+                if (key >= a.s_local) st[cb][r] = -INFINITY;
+                tmax = fmaxf(tmax, st[cb][r]);
             }
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        const float m_new = fmaxf(m, tmax);        // finite: every tile has a key
-        const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+        const float m_new = fmaxf(m, tmax * a.scale_log2);   // finite: every tile has a key
         float psum = 0.0f;
         bf16x8 pb[4];                               // P^T operands, keys as above
 #pragma unroll
         for (int kg = 0; kg < 4; ++kg)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float p = __builtin_amdgcn_exp2f(st[kg >> 1][8 * (kg & 1) + e] - m_new);
+                const float p =
+                    __builtin_amdgcn_exp2f(fmaf(st[kg >> 1][8 * (kg & 1) + e], a.scale_log2, -m_new));
                 psum += p;
                 pb[kg][e] = (__bf16)p;
             }
         psum += __shfl_xor(psum, 32);
-        l = l * alpha + psum;
+        // Rescale O only when some query of the wave has a new maximum.
+        if (__builtin_amdgcn_ballot_w64(m_new != m) != 0) {
+            const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+            l *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+        }
+        l += psum;
         m = m_new;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
 
         // O^T += V^T P^T.  Product kg covers keys 32*(kg/2) + 16*(kg%2) + {4g..4g+3,
         // 8+4g..8+4g+3} for lane group g: the keys its P^T operand holds.

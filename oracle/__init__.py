@@ -83,7 +83,7 @@ def load(path):
     L.spo_f32_to_bf16.restype = ctypes.c_uint16
     L.spo_bf16_to_f32.argtypes = [ctypes.c_uint16]
     L.spo_bf16_to_f32.restype = ctypes.c_float
-    L.spo_attention.argtypes = [ctypes.POINTER(spo_attn_desc), P, P, P, P, P]
+    L.spo_attention.argtypes = [ctypes.POINTER(spo_attn_desc), I64, I64, P, P, P, P, P]
     L.spo_attention.restype = ctypes.c_int
     L.spo_reduce_parts.argtypes = [D, ctypes.c_int, P, P]
     L.spo_reduce_parts.restype = ctypes.c_int
@@ -176,18 +176,21 @@ class AttnDesc:
         return spo_attn_desc(self.s_local, self.b, self.heads, self.d, self.t, self.rank, sc)
 
 
-def attention(d, q, k, v, L=None):
+def attention(d, q, k, v, rows=None, L=None):
     """Ordinary attention of the rank's queries over the keys of all t
-    blocks, float64.  q: s_local*b*heads*d bf16 bits; k, v: t times that.
-    Returns (o float64 [s_local*b*heads*d], lse float64 [s_local*b*heads])."""
+    blocks, float64.  q: the query tokens [r0, r1) (default: all s_local)
+    as bf16 bits; k, v: all t blocks.  Returns (o float64, lse float64) for
+    those queries."""
     L = L or lib()
-    n = d.s_local * d.b * d.heads * d.d
-    q = _check(q, np.uint16, n, "q")
-    k = _check(k, np.uint16, d.t * n, "k")
-    v = _check(v, np.uint16, d.t * n, "v")
-    o = np.empty(n, np.float64)
-    lse = np.empty(d.s_local * d.b * d.heads, np.float64)
-    if L.spo_attention(ctypes.byref(d.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse)) != 0:
+    r0, r1 = rows if rows is not None else (0, d.s_local)
+    tok = d.b * d.heads * d.d
+    q = _check(q, np.uint16, (r1 - r0) * tok, "q")
+    k = _check(k, np.uint16, d.t * d.s_local * tok, "k")
+    v = _check(v, np.uint16, d.t * d.s_local * tok, "v")
+    o = np.empty((r1 - r0) * tok, np.float64)
+    lse = np.empty((r1 - r0) * d.b * d.heads, np.float64)
+    if L.spo_attention(ctypes.byref(d.c()), r0, r1, _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                       _ptr(lse)) != 0:
         raise ValueError("spo_attention rejected its arguments")
     return o, lse
 

@@ -486,10 +486,11 @@ void spo_layer_activation_elems(double s, double b, double h, double a, double t
 /* ------------------------------------------------------------------------ */
 /* Ring attention: ordinary attention over all keys (see the header)         */
 /* ------------------------------------------------------------------------ */
-int spo_attention(const spo_attn_desc* d, const uint16_t* q, const uint16_t* k,
-                  const uint16_t* v, double* o_out, double* lse_out)
+int spo_attention(const spo_attn_desc* d, int64_t r0, int64_t r1, const uint16_t* q,
+                  const uint16_t* k, const uint16_t* v, double* o_out, double* lse_out)
 {
     if (!d || !q || !k || !v || !o_out || !lse_out) return -1;
+    if (r0 < 0 || r1 < r0 || r1 > d->s_local) return -1;
     if (d->s_local < 1 || d->b < 1 || d->heads < 1 || d->d < 1 || d->t < 1) return -1;
     if (d->rank < 0 || d->rank >= d->t || !(d->scale > 0.0f)) return -1;
     const int64_t S = d->s_local, B = d->b, NH = d->heads, D = d->d;
@@ -498,7 +499,7 @@ int spo_attention(const spo_attn_desc* d, const uint16_t* q, const uint16_t* k,
     if (!s) return -1;
     /* element (token, batch, head, dim) of a [tokens][b][heads][d] tensor */
 #define AT(tok, bi, hh, dd) ((((tok) * B + (bi)) * NH + (hh)) * D + (dd))
-    for (int64_t qi = 0; qi < S; ++qi)
+    for (int64_t qi = 0; qi < r1 - r0; ++qi)                    /* query token r0 + qi */
         for (int64_t bi = 0; bi < B; ++bi)
             for (int64_t hh = 0; hh < NH; ++hh) {
                 double m = -INFINITY;

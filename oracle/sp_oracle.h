@@ -169,9 +169,10 @@ void spo_layer_activation_elems(double s, double b, double h, double a, double t
  * over the keys j of all t blocks with the query's batch index and head.
  * Layouts (bf16 as raw 16-bit words): q [s_local][b][heads][d]; k and v
  * [t][s_local][b][heads][d] (block j = the tokens of rank j); o_out
- * [s_local][b][heads][d] and lse_out [s_local][b][heads] in float64.  rank
- * does not change the result (it orders the ring).  Returns 0, or -1 on an
- * invalid argument.
+ * [s_local][b][heads][d] and lse_out [s_local][b][heads] in float64.  Only
+ * the rank's query tokens [r0, r1) are computed: q, o_out and lse_out start
+ * at token r0 (as the region's row ranges).  rank does not change the result
+ * (it orders the ring).  Returns 0, or -1 on an invalid argument.
  * Parity: pinned (torch float64 scaled_dot_product_attention, a single key,
  * identical keys, constant values, a two-key closed form, invariance to the
  * order of the key blocks). */
@@ -185,8 +186,8 @@ typedef struct {
     float   scale;     /* softmax scale, usually 1/sqrt(d)                 */
 } spo_attn_desc;
 
-int spo_attention(const spo_attn_desc* d, const uint16_t* q, const uint16_t* k,
-                  const uint16_t* v, double* o_out, double* lse_out);
+int spo_attention(const spo_attn_desc* d, int64_t r0, int64_t r1, const uint16_t* q,
+                  const uint16_t* k, const uint16_t* v, double* o_out, double* lse_out);
 
 #ifdef __cplusplus
 }

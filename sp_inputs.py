@@ -130,3 +130,38 @@ WORKLOADS = {
 }
 
 HEADLINE = "22b_h6144_t8"
+
+
+@dataclass
+class AttnWorkload:
+    """One rank of a ring-attention forward: s tokens split over t ranks,
+    `heads` heads of width d on this GPU (the model's heads divided by the
+    tensor-parallel degree)."""
+    name: str
+    s: int
+    t: int
+    b: int
+    heads: int
+    d: int
+    seed: int = 0
+
+    @property
+    def s_local(self):
+        return self.s // self.t
+
+    @property
+    def flops(self):
+        """Multiply-adds x 2 of Q K^T and P V over all keys."""
+        return 4 * self.s_local * self.s * self.b * self.heads * self.d
+
+
+ATTN_WORKLOADS = {
+    # The long-sequence configuration's attention core under context
+    # parallelism: s = 32768 over t = 8 ranks, h = 8192 = 64 heads of 128,
+    # 8 of them per GPU (tensor-parallel degree 8).
+    "ring_attn_s32k_t8_h8192": AttnWorkload("ring_attn_s32k_t8_h8192", s=32768, t=8, b=1,
+                                            heads=8, d=128),
+    # The same heads at the 22B layer's length: s = 2048 over t = 8.
+    "ring_attn_s2k_t8_d128": AttnWorkload("ring_attn_s2k_t8_d128", s=2048, t=8, b=4, heads=8,
+                                          d=128),
+}

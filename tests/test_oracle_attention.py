@@ -102,6 +102,19 @@ def test_result_does_not_depend_on_the_ring_order(olib):
         assert np.allclose(lse, ref[1], rtol=0, atol=1e-13)
 
 
+def test_query_ranges_concatenate(olib):
+    s_local, b, heads, dim, t = 6, 2, 2, 16, 2
+    d = oracle.AttnDesc(s_local=s_local, b=b, heads=heads, d=dim, t=t)
+    x = make_attn_inputs(s_local, b, heads, dim, t, seed=8)
+    o, lse = oracle.attention(d, x["q"], x["k"], x["v"], L=olib)
+    tok = b * heads * dim
+    for r0, r1 in ((0, 2), (2, 5), (5, 6)):
+        oo, ll = oracle.attention(d, x["q"][r0 * tok:r1 * tok], x["k"], x["v"], rows=(r0, r1),
+                                  L=olib)
+        assert np.array_equal(oo, o[r0 * tok:r1 * tok])
+        assert np.array_equal(ll, lse[r0 * b * heads:r1 * b * heads])
+
+
 def test_rejects_bad_arguments(olib):
     x = make_attn_inputs(2, 1, 1, 8, 2, seed=1)
     with pytest.raises(ValueError):
