@@ -57,6 +57,12 @@ struct AttnArgs {
 constexpr int kQT = 128;   // queries per workgroup (4 waves x 32)
 constexpr int kKT = 64;    // keys per tile
 
+// Column swizzle of the transposed V tile: key k of row d is stored at
+// column k ^ vswz(d).  Rows 8 apart (the rows one staging instruction's lanes
+// write) would otherwise fall in the same LDS bank; the XOR is a multiple of
+// 4 keys, so the 4-key runs that are written and read stay contiguous.
+__device__ __forceinline__ int vswz(int row) { return 4 * ((row >> 3) & 15); }
+
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -70,8 +76,10 @@ __global__ void __launch_bounds__(256, 2) ring_attn_step_kernel(AttnArgs a) {
     constexpr int CH = kKT * D / 8;     // 16-byte chunks per K (or V) tile
     constexpr int CPT = CH / 256;       // chunks per thread
     static_assert(CH % 256 == 0, "tile chunks must split evenly over the workgroup");
-    __shared__ __attribute__((aligned(16))) __bf16 ks[kKT * KP];   // K tile [key][d]
-    __shared__ __attribute__((aligned(16))) __bf16 vt[D * VP];     // V tile [d][key]
+    // Two buffers of (K tile [key][d], V tile transposed [d][key]): the next
+    // tile is staged into one while the other is read, one barrier a tile.
+    extern __shared__ __attribute__((aligned(16))) __bf16 lds[];
+    constexpr int KSZ = kKT * KP, BUF = kKT * KP + D * VP;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 5, c = lane & 31;
@@ -115,7 +123,9 @@ __global__ void __launch_bounds__(256, 2) ring_attn_step_kernel(AttnArgs a) {
             vn[i] = load_stream(vb + vk * tok + 8 * vdc);
         }
     };
-    auto stage = [&]() {
+    auto stage = [&](int buf) {
+        __bf16* ks = lds + buf * BUF;
+        __bf16* vt = ks + KSZ;
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
             const int cc = tid + 256 * i, key = cc / (D / 8), dc = cc % (D / 8);
@@ -129,12 +139,13 @@ __global__ void __launch_bounds__(256, 2) ring_attn_step_kernel(AttnArgs a) {
             for (int j = 0; j < R; ++j) v8[j] = __builtin_bit_cast(bf16x8, vn[R * iu + j]);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
+                const int row = 8 * vdc + e, col = vkey ^ vswz(row);
                 if constexpr (R == 4) {
                     const bf16x4 run = {v8[0][e], v8[1][e], v8[2][e], v8[3][e]};
-                    *reinterpret_cast<bf16x4*>(&vt[(8 * vdc + e) * VP + vkey]) = run;
+                    *reinterpret_cast<bf16x4*>(&vt[row * VP + col]) = run;
                 } else {
                     const bf16x2 run = {v8[0][e], v8[1][e]};
-                    *reinterpret_cast<bf16x2*>(&vt[(8 * vdc + e) * VP + vkey]) = run;
+                    *reinterpret_cast<bf16x2*>(&vt[row * VP + col]) = run;
                 }
             }
         }
@@ -148,36 +159,45 @@ __global__ void __launch_bounds__(256, 2) ring_attn_step_kernel(AttnArgs a) {
     float m = -INFINITY, l = 0.0f;      // running max (base-2 units) and sum of this query
 
     fetch(0);
+    stage(0);
+    __syncthreads();
+    if (kKT < a.s_local) fetch(kKT);
+    int cur = 0;
     for (int64_t k0 = 0; k0 < a.s_local; k0 += kKT) {
-        __syncthreads();                // every wave is done with the previous tile
-        stage();
-        __syncthreads();
-        if (k0 + kKT < a.s_local) fetch(k0 + kKT);
+        const __bf16* ks = lds + cur * BUF;
+        const __bf16* vt = ks + KSZ;
 
         // S^T = K Q^T for keys 32*cb .. 32*cb+31 of the tile.
+        // The two blocks' products alternate, so consecutive MFMAs are independent.
         f32x16 st[2];
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
+        for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) st[cb][r] = 0.0f;
 #pragma unroll
-            for (int s = 0; s < KS; ++s) {
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) {
                 const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&ks[(32 * cb + c) * KP + 16 * s + 8 * g]);
                 st[cb] = mfma32(ka, qv[s], st[cb]);
             }
-        }
         // Register r of block cb holds key 32*cb + 8*(r/4) + 4*g + r%4.  The
         // max is taken on the raw scores (the scale is positive) and the
         // scale enters through the exponent's FMA: p = 2^(s*c - m).
+        if (k0 + kKT > a.s_local) {          // the last, ragged tile (uniform)
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int64_t key = k0 + 32 * cb + 8 * (r / 4) + 4 * g + (r % 4);
+                    if (key >= a.s_local) st[cb][r] = -INFINITY;
+                }
+        }
         float tmax = -INFINITY;
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t key = k0 + 32 * cb + 8 * (r / 4) + 4 * g + (r % 4);
-                if (key >= a.s_local) st[cb][r] = -INFINITY;
-                tmax = fmaxf(tmax, st[cb][r]);
-            }
+            for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, st[cb][r]);
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
         const float m_new = fmaxf(m, tmax * a.scale_log2);   // finite: every tile has a key
         float psum = 0.0f;
@@ -211,13 +231,18 @@ __global__ void __launch_bounds__(256, 2) ring_attn_step_kernel(AttnArgs a) {
             const int kbase = 32 * (kg >> 1) + 16 * (kg & 1) + 4 * g;
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                const __bf16* vr = &vt[(32 * db + c) * VP + kbase];
-                const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vr);
-                const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vr + 8);
+                const int row = 32 * db + c, sw = vswz(row);
+                const bf16x4 lo = *reinterpret_cast<const bf16x4*>(&vt[row * VP + (kbase ^ sw)]);
+                const bf16x4 hi =
+                    *reinterpret_cast<const bf16x4*>(&vt[row * VP + ((kbase + 8) ^ sw)]);
                 const bf16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                 o[db] = mfma32(va, pb[kg], o[db]);
             }
         }
+        if (k0 + kKT < a.s_local) stage(cur ^ 1);   // the next tile, fetched a tile ago
+        __syncthreads();            // staged tile visible; every wave is done with `cur`
+        if (k0 + 2 * kKT < a.s_local) fetch(k0 + 2 * kKT);
+        cur ^= 1;
     }
 
     // The step's partial: O / l and its log-sum-exp (natural log).
@@ -271,8 +296,12 @@ template <int D>
 static hipError_t launch_attn(const AttnArgs& a, int steps, bool merge, hipStream_t s) {
     const dim3 g((unsigned)((a.s_local + kQT - 1) / kQT), (unsigned)(a.b * a.heads),
                  (unsigned)steps);
-    hipLaunchKernelGGL(ring_attn_step_kernel<D>, g, dim3(256), 0, s, a);
-    hipError_t e = hipGetLastError();
+    constexpr size_t lds = 2 * ((size_t)kKT * (D + 8) + (size_t)D * (kKT + 8)) * sizeof(__bf16);
+    hipError_t e = hipFuncSetAttribute((const void*)ring_attn_step_kernel<D>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(ring_attn_step_kernel<D>, g, dim3(256), lds, s, a);
+    e = hipGetLastError();
     if (e != hipSuccess || !merge) return e;
     const int64_t nrows = a.s_local * a.b * a.heads;
     const int64_t rpb = 256 / (D / 4);
