@@ -36,12 +36,20 @@ PROFILES = os.path.join(ROOT, "profiles")
 COPY_BYTES = 1 << 30             # the plain copy the counters are calibrated on
 
 
-def kernel_source_hash():
-    """Hash of the HIP sources: counter figures taken on other sources are stale."""
+# The HIP sources each workload family runs: counter figures taken on other
+# sources are stale.
+REGION_SOURCES = ("sp_device.h", "sp_plan.h", "sp_host_checks.h", "sp_fwd.hip", "sp_bwd.hip",
+                  "sp_region_api.hip")
+ATTN_SOURCES = ("sp_device.h", "sp_host_checks.h", "ring_attn.hip")
+
+
+def kernel_source_hash(workload=None):
+    from sp_inputs import ATTN_WORKLOADS
+    names = ATTN_SOURCES if workload in ATTN_WORKLOADS else REGION_SOURCES
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "dropout_region_amd", "csrc", "*"))):
-        h.update(os.path.basename(f).encode())
-        h.update(open(f, "rb").read())
+    for n in names:
+        h.update(n.encode())
+        h.update(open(os.path.join(ROOT, "dropout_region_amd", "csrc", n), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -135,14 +143,16 @@ def copy_bandwidth(torch, nbytes=COPY_BYTES, iters=20):
 
 # ------------------------------------------------------------------ summaries
 def _profile_name(workload, what):
-    return os.path.join(PROFILES, f"sp_region_{workload}_{what}")
+    prefix = "" if workload.startswith("ring_attn") else "sp_region_"
+    return os.path.join(PROFILES, f"{prefix}{workload}_{what}")
 
 
 def _short(name):
     """Readable kernel name: sp_region_fwd_kernel etc. (template arguments dropped)."""
     for base in ("sp_region_fwd_kernel", "sp_region_fwd_stream_kernel", "sp_region_bwd_rows_kernel",
                  "sp_region_bwd_rowsum_kernel", "sp_region_bwd_main_kernel",
-                 "sp_region_bwd_finalize_kernel"):
+                 "sp_region_bwd_finalize_kernel", "sp_region_bwd_exit_kernel",
+                 "ring_attn_step_kernel", "ring_attn_merge_kernel"):
         if base in name:
             return base
     return name
@@ -163,7 +173,7 @@ def pmc_summary(fetch_dir, write_dir, workload, command):
     copy_name = [k for k in fetch if "copyBuffer" in k][0]
     f_scale = COPY_BYTES / max(fetch[copy_name])
     w_scale = COPY_BYTES / max(write[copy_name])
-    out = {"command": command, "source_hash": kernel_source_hash(), "workload": workload,
+    out = {"command": command, "source_hash": kernel_source_hash(workload), "workload": workload,
            "copy_kernel": copy_name, "copy_bytes": COPY_BYTES,
            "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4), "kernels": {}}
     for k in fetch:
@@ -183,13 +193,37 @@ def stats_summary(trace_dir, workload, command):
     rows = list(csv.DictReader(open(glob.glob(os.path.join(trace_dir, "*kernel_stats.csv"))[0])))
     lines = [f"# rocprofv3 kernel statistics: {workload}", "",
              "Command (from the repository root, on the GPU box):", "", "```", command, "```", "",
-             f"Kernel sources: `{kernel_source_hash()}` (hash of dropout_region_amd/csrc/*)", "",
+             f"Kernel sources: `{kernel_source_hash(workload)}` (hash of the workload's files in "
+             "dropout_region_amd/csrc)", "",
              "| Kernel | Calls | Average ns | Min ns | Max ns | Share % |", "|---|---|---|---|---|---|"]
     for r in rows:
         lines.append(f"| {_short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']):.0f} | "
                      f"{float(r['MinNs']):.0f} | {float(r['MaxNs']):.0f} | "
                      f"{float(r['Percentage']):.2f} |")
     path = _profile_name(workload, "kernel_stats.md")
+    open(path, "w").write("\n".join(lines) + "\n")
+    print(path)
+
+
+def counters_summary(pmc_dir, workload, command):
+    """Markdown table of the counters of a rocprofv3 --pmc run, averaged per
+    dispatch for each kernel of the workload."""
+    rows = list(csv.DictReader(open(glob.glob(os.path.join(pmc_dir, "*counter_collection.csv"))[0])))
+    by = {}
+    for r in rows:
+        k = _short(r["Kernel_Name"])
+        if not (k.startswith("sp_region") or k.startswith("ring_attn")):
+            continue
+        by.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    lines = [f"# rocprofv3 counters: {workload}", "", "Command (from the repository root, on the GPU box):",
+             "", "```", command, "```", "",
+             f"Kernel sources: `{kernel_source_hash(workload)}` (hash of the workload's files in "
+             "dropout_region_amd/csrc)", "", "Average per dispatch.", ""]
+    for k, cs in by.items():
+        lines += [f"## {k}", "", "| Counter | Value |", "|---|---|"]
+        lines += [f"| {c} | {sum(v) / len(v):.6g} |" for c, v in sorted(cs.items())]
+        lines.append("")
+    path = _profile_name(workload, "counters.md")
     open(path, "w").write("\n".join(lines) + "\n")
     print(path)
 
@@ -201,7 +235,7 @@ def load_traffic(workload):
     if not os.path.exists(path):
         return None
     t = json.load(open(path))
-    return t["kernels"] if t.get("source_hash") == kernel_source_hash() else None
+    return t["kernels"] if t.get("source_hash") == kernel_source_hash(workload) else None
 
 
 # ------------------------------------------------------------------ ring attention
@@ -331,6 +365,7 @@ def main():
                          "regenerates the dropout decisions")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--stats-summary", metavar="TRACE_DIR")
+    ap.add_argument("--counters-summary", metavar="PMC_DIR")
     ap.add_argument("--command", default="", help="command recorded in a summary")
     args = ap.parse_args()
 
@@ -340,6 +375,8 @@ def main():
         return pmc_summary(*args.pmc_summary, wname, args.command)
     if args.stats_summary:
         return stats_summary(args.stats_summary, wname, args.command)
+    if args.counters_summary:
+        return counters_summary(args.counters_summary, wname, args.command)
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
               "(the region is per-rank; there are no collectives to run)", file=sys.stderr)
