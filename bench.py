@@ -192,7 +192,7 @@ def stats_summary(trace_dir, workload, command):
     """Markdown table of a rocprofv3 --kernel-trace --stats run."""
     rows = list(csv.DictReader(open(glob.glob(os.path.join(trace_dir, "*kernel_stats.csv"))[0])))
     lines = [f"# rocprofv3 kernel statistics: {workload}", "",
-             "Command (from the repository root, on the GPU box):", "", "```", command, "```", "",
+             "Command (from the repository root, on the MI355X host):", "", "```", command, "```", "",
              f"Kernel sources: `{kernel_source_hash(workload)}` (hash of the workload's files in "
              "dropout_region_amd/csrc)", "",
              "| Kernel | Calls | Average ns | Min ns | Max ns | Share % |", "|---|---|---|---|---|---|"]
@@ -215,7 +215,7 @@ def counters_summary(pmc_dir, workload, command):
         if not (k.startswith("sp_region") or k.startswith("ring_attn")):
             continue
         by.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
-    lines = [f"# rocprofv3 counters: {workload}", "", "Command (from the repository root, on the GPU box):",
+    lines = [f"# rocprofv3 counters: {workload}", "", "Command (from the repository root, on the MI355X host):",
              "", "```", command, "```", "",
              f"Kernel sources: `{kernel_source_hash(workload)}` (hash of the workload's files in "
              "dropout_region_amd/csrc)", "", "Average per dispatch.", ""]

@@ -2,7 +2,7 @@
 
 Masks and h must be bit-exact; y, the statistics and the gradients must meet
 the tolerances in tests/parity.py.  Every backward check feeds both sides the
-oracle's saved tensors (so the backward is judged alone), runs the GPU call
+oracle's saved tensors (so the backward is checked alone), runs the GPU call
 twice into the same buffers (results must be bit-identical), and also runs
 the GPU backward from the GPU forward's own saved tensors (the chain).
 """
