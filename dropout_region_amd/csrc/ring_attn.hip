@@ -56,6 +56,7 @@ struct AttnArgs {
 
 constexpr int kQT = 128;   // queries per workgroup (4 waves x 32)
 constexpr int kKT = 64;    // keys per tile
+constexpr float kStale = 8.0f;   // base-2 headroom before the softmax reference moves
 
 // Column swizzle of the transposed V tile: key k of row d is stored at
 // column k ^ vswz(d).  Rows 8 apart (the rows one staging instruction's lanes
@@ -110,17 +111,35 @@ __global__ void __launch_bounds__(256, 2) ring_attn_step_kernel(AttnArgs a) {
     constexpr int R = CPT >= 4 ? 4 : CPT;
     static_assert(CPT % R == 0 && (R == 2 || R == 4), "V is staged in runs of 2 or 4 keys");
     uint4 kn[CPT], vn[CPT];
-    auto fetch = [&](int64_t k0) {
+    // Per-thread byte offsets inside a tile (the tile's base is uniform).
+    uint32_t koff[CPT], voff[CPT];
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int cc = tid + 256 * i, key = cc / (D / 8), dc = cc % (D / 8);
-            const int64_t kk = k0 + key < a.s_local ? k0 + key : a.s_local - 1;   // clamp
-            kn[i] = load_stream(kb + kk * tok + 8 * dc);
-            // V: unit u = tid + 256*(i/R) -> d chunk u % (D/8), key group u / (D/8),
-            // key R*group + i%R
-            const int u = tid + 256 * (i / R), vdc = u % (D / 8), vkey = R * (u / (D / 8)) + (i % R);
-            const int64_t vk = k0 + vkey < a.s_local ? k0 + vkey : a.s_local - 1;
-            vn[i] = load_stream(vb + vk * tok + 8 * vdc);
+    for (int i = 0; i < CPT; ++i) {
+        const int cc = tid + 256 * i, key = cc / (D / 8), dc = cc % (D / 8);
+        koff[i] = (uint32_t)(key * tok + 8 * dc) * 2u;
+        const int u = tid + 256 * (i / R), vdc = u % (D / 8), vkey = R * (u / (D / 8)) + (i % R);
+        voff[i] = (uint32_t)(vkey * tok + 8 * vdc) * 2u;
+    }
+    auto fetch = [&](int64_t k0) {
+        const char* kt = reinterpret_cast<const char*>(kb + k0 * tok);
+        const char* vt0 = reinterpret_cast<const char*>(vb + k0 * tok);
+        if (k0 + kKT <= a.s_local) {                 // a whole tile (uniform)
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) {
+                kn[i] = load_stream(kt + koff[i]);
+                vn[i] = load_stream(vt0 + voff[i]);
+            }
+        } else {                                     // the ragged last tile: clamp
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) {
+                const int cc = tid + 256 * i, key = cc / (D / 8), dc = cc % (D / 8);
+                const int64_t kk = k0 + key < a.s_local ? k0 + key : a.s_local - 1;
+                kn[i] = load_stream(kb + kk * tok + 8 * dc);
+                const int u = tid + 256 * (i / R), vdc = u % (D / 8);
+                const int vkey = R * (u / (D / 8)) + (i % R);
+                const int64_t vk = k0 + vkey < a.s_local ? k0 + vkey : a.s_local - 1;
+                vn[i] = load_stream(vb + vk * tok + 8 * vdc);
+            }
         }
     };
     auto stage = [&](int buf) {
@@ -137,15 +156,16 @@ __global__ void __launch_bounds__(256, 2) ring_attn_step_kernel(AttnArgs a) {
             bf16x8 v8[R];
 #pragma unroll
             for (int j = 0; j < R; ++j) v8[j] = __builtin_bit_cast(bf16x8, vn[R * iu + j]);
+            // rows 8*vdc + e share vswz (= 4*(vdc % 16)): one column for all e
+            __bf16* vrow = &vt[8 * vdc * VP + (vkey ^ vswz(8 * vdc))];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const int row = 8 * vdc + e, col = vkey ^ vswz(row);
                 if constexpr (R == 4) {
                     const bf16x4 run = {v8[0][e], v8[1][e], v8[2][e], v8[3][e]};
-                    *reinterpret_cast<bf16x4*>(&vt[row * VP + col]) = run;
+                    *reinterpret_cast<bf16x4*>(vrow + e * VP) = run;
                 } else {
                     const bf16x2 run = {v8[0][e], v8[1][e]};
-                    *reinterpret_cast<bf16x2*>(&vt[row * VP + col]) = run;
+                    *reinterpret_cast<bf16x2*>(vrow + e * VP) = run;
                 }
             }
         }
@@ -158,6 +178,7 @@ __global__ void __launch_bounds__(256, 2) ring_attn_step_kernel(AttnArgs a) {
         for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
     float m = -INFINITY, l = 0.0f;      // running max (base-2 units) and sum of this query
 
+    const int vcol = (4 * g) ^ (4 * (c >> 3));     // lane part of the V^T read column
     fetch(0);
     stage(0);
     __syncthreads();
@@ -165,7 +186,7 @@ __global__ void __launch_bounds__(256, 2) ring_attn_step_kernel(AttnArgs a) {
     int cur = 0;
     for (int64_t k0 = 0; k0 < a.s_local; k0 += kKT) {
         const __bf16* ks = lds + cur * BUF;
-        const __bf16* vt = ks + KSZ;
+        const __bf16* vlane = ks + KSZ + c * VP;
 
         // S^T = K Q^T for keys 32*cb .. 32*cb+31 of the tile.
         // The two blocks' products alternate, so consecutive MFMAs are independent.
@@ -199,7 +220,12 @@ __global__ void __launch_bounds__(256, 2) ring_attn_step_kernel(AttnArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, st[cb][r]);
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        const float m_new = fmaxf(m, tmax * a.scale_log2);   // finite: every tile has a key
+        // The reference m moves only when a score exceeds it by more than
+        // 2^kStale: the probabilities 2^(s*c - m) stay below 2^kStale (fine in
+        // bf16 and in the fp32 sums), O / l and m + log2(l) do not depend on
+        // which m is used, and the O rescale is skipped in nearly every tile.
+        const float mt = tmax * a.scale_log2;                // finite: every tile has a key
+        const float m_new = mt > m + kStale ? mt : m;
         float psum = 0.0f;
         bf16x8 pb[4];                               // P^T operands, keys as above
 #pragma unroll
@@ -226,15 +252,17 @@ __global__ void __launch_bounds__(256, 2) ring_attn_step_kernel(AttnArgs a) {
 
         // O^T += V^T P^T.  Product kg covers keys 32*(kg/2) + 16*(kg%2) + {4g..4g+3,
         // 8+4g..8+4g+3} for lane group g: the keys its P^T operand holds.
+        // (kbase ^ vswz(row)) with kbase = 32*(kg/2) + 16*(kg%2) + 4*g and
+        // row = 32*db + c splits into a lane part in bits 2-3, 4*g ^ 4*(c/8),
+        // and a part in bits 4-5 known at compile time; kbase + 8 flips bit 3.
 #pragma unroll
         for (int kg = 0; kg < 4; ++kg) {
-            const int kbase = 32 * (kg >> 1) + 16 * (kg & 1) + 4 * g;
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                const int row = 32 * db + c, sw = vswz(row);
-                const bf16x4 lo = *reinterpret_cast<const bf16x4*>(&vt[row * VP + (kbase ^ sw)]);
-                const bf16x4 hi =
-                    *reinterpret_cast<const bf16x4*>(&vt[row * VP + ((kbase + 8) ^ sw)]);
+                const int ct = (32 * (kg >> 1) + 16 * (kg & 1)) ^ (16 * (db & 3));
+                const __bf16* vr = vlane + 32 * db * VP + ct;
+                const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vr + vcol);
+                const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vr + (vcol ^ 8));
                 const bf16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                 o[db] = mfma32(va, pb[kg], o[db]);
             }
