@@ -1,0 +1,53 @@
+"""The benchmark's algorithmic byte and FLOP counts, from the element sizes
+(no GPU).  Forward: read x and residual, write h and y (2 bytes each for
+bf16, 4 for fp32), one mask byte per element when p > 0, bias/gamma/beta
+read once per call, fp32 statistics per row.  Backward: read dy and h, the
+mask, write dx and dresidual, read gamma and the statistics, write the three
+parameter gradients."""
+import pytest
+
+import bench
+from sp_inputs import ATTN_WORKLOADS, WORKLOADS
+
+
+@pytest.mark.parametrize("name,fwd,bwd", [
+    # 22B: [256, 4, 6144] bf16 LayerNorm p = 0.1
+    ("22b_h6144_t8", 6291456 * 9 + 3 * 6144 * 4 + 2 * 1024 * 4,
+     6291456 * 9 + 2 * 1024 * 4 + 6144 * 4 + 3 * 6144 * 4),
+    # 175B: [256, 8, 12288], one call
+    ("175b_h12288_t8", 25165824 * 9 + 3 * 12288 * 4 + 2 * 2048 * 4,
+     25165824 * 9 + 2 * 2048 * 4 + 12288 * 4 + 3 * 12288 * 4),
+    # long-sequence RMSNorm [4096, 1, 8192]: no beta, one statistic
+    ("longseq_rms_h8192_t8_p0.1", 33554432 * 9 + 2 * 8192 * 4 + 4096 * 4,
+     33554432 * 9 + 4096 * 4 + 8192 * 4 + 2 * 8192 * 4),
+    ("longseq_rms_h8192_t8_p0", 33554432 * 8 + 2 * 8192 * 4 + 4096 * 4,
+     33554432 * 8 + 4096 * 4 + 8192 * 4 + 2 * 8192 * 4),
+    # tiny fp32 [64, 2, 256]: 4 bytes per element
+    ("tiny_fp32_t2", 32768 * 17 + 3 * 256 * 4 + 2 * 128 * 4,
+     32768 * 17 + 2 * 128 * 4 + 256 * 4 + 3 * 256 * 4),
+])
+def test_region_bytes(name, fwd, bwd):
+    f, r, g = bench.algorithmic_bytes(WORKLOADS[name])
+    assert f == fwd and r + g == bwd
+
+
+def test_region_byte_variants():
+    w = WORKLOADS["22b_h6144_t8"]
+    E, H, N = w.elems, w.h, w.rows
+    f, r, g = bench.algorithmic_bytes(w, with_dh_out=True)
+    assert r == E * 11 + 2 * N * 4 + H * 4                 # dh_out read too
+    f, r, g = bench.algorithmic_bytes(w, mask_stored=False)
+    assert f == E * 8 + 3 * H * 4 + 2 * N * 4               # no mask written or read
+    f, r, g = bench.algorithmic_bytes(w, x_parts=8)
+    assert f == E * ((8 + 3) * 2 + 1) + 3 * H * 4 + 2 * N * 4   # eight slabs of x read
+    fe, be = bench.variant_bytes(w, "entry")
+    assert fe == E * 4 + 2 * H * 4 + 2 * N * 4              # residual in, y out
+    fx, bx = bench.variant_bytes(w, "exit")
+    assert fx == E * 7 + H * 4 and bx == E * 5 + H * 4      # x, res in, h, mask out / dh, mask in, dx out
+
+
+def test_attention_flops():
+    w = ATTN_WORKLOADS["ring_attn_s32k_t8_h8192"]
+    assert w.s_local == 4096
+    # Q K^T and P V over 32768 keys: 2 * 2 * 4096 * 32768 * 128 per head, 8 heads
+    assert w.flops == 4 * 4096 * 32768 * 128 * 8 == 549755813888
