@@ -28,6 +28,8 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <atomic>
+
 #include "sp_device.h"
 #include "sp_host_checks.h"
 #include "sp_ring_attn.h"
@@ -325,9 +327,18 @@ static hipError_t launch_attn(const AttnArgs& a, int steps, bool merge, hipStrea
     const dim3 g((unsigned)((a.s_local + kQT - 1) / kQT), (unsigned)(a.b * a.heads),
                  (unsigned)steps);
     constexpr size_t lds = 2 * ((size_t)kKT * (D + 8) + (size_t)D * (kKT + 8)) * sizeof(__bf16);
-    hipError_t e = hipFuncSetAttribute((const void*)ring_attn_step_kernel<D>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    // The dynamic LDS allowance is set once per device (bit d of `done`).
+    static std::atomic<uint64_t> done{0};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
+    const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
+    if (!bit || !(done.load(std::memory_order_acquire) & bit)) {
+        e = hipFuncSetAttribute((const void*)ring_attn_step_kernel<D>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        done.fetch_or(bit, std::memory_order_release);
+    }
     hipLaunchKernelGGL(ring_attn_step_kernel<D>, g, dim3(256), lds, s, a);
     e = hipGetLastError();
     if (e != hipSuccess || !merge) return e;
