@@ -224,3 +224,26 @@ def test_ring_attn_rejects_bad_calls(L):
                                                            for i in range(3)],
                                    ctypes.c_void_p(A + 0x8000000), ctypes.c_size_t(need),
                                    None) == spr.SPR_ERR_INVALID_ARG
+
+
+def test_activation_bytes_count_the_buffers_a_forward_keeps(L):
+    """The bytes of the buffers a forward call writes and keeps (h, mask,
+    statistics for the backward; y for the next block), as allocated for the
+    call, equal sp_region_activation_bytes; two calls per layer give the
+    replicated band divided by t, 10*s*b*h/t bytes plus the statistics."""
+    import torch
+    from sp_inputs import WORKLOADS
+    for name, w in WORKLOADS.items():
+        d = spr.Desc(s_local=w.s_local, b=w.b, h=w.h, t=w.t, io=w.io, norm=w.norm, p=w.p,
+                     eps=w.eps)
+        o = spr.alloc_fwd_outputs(d, torch.device("meta"))
+        nbytes = lambda k: 0 if o[k] is None else o[k].numel() * o[k].element_size()
+        saved = nbytes("h") + nbytes("mask") + nbytes("mean") + nbytes("rstd")
+        assert spr.sp_region_activation_bytes(d) == (saved, nbytes("y")), name
+        if name.startswith("1t_"):
+            stats = 2 * 8 * w.rows
+            assert 2 * (saved + nbytes("y")) - stats == 10 * w.s * w.b * w.h // w.t, name
+        free = spr.alloc_fwd_outputs(d, torch.device("meta"), store_mask=False)
+        kept = sum(0 if free[k] is None else free[k].numel() * free[k].element_size()
+                   for k in ("h", "mask", "mean", "rstd"))
+        assert saved - kept == (w.rows * w.h if w.p > 0 else 0), name
