@@ -56,7 +56,6 @@ struct AttnArgs {
     float scale_log2;      // softmax scale * log2(e): scores in base-2 units
 };
 
-constexpr int kQT = 128;   // queries per workgroup (4 waves x 32)
 constexpr int kKT = 64;    // keys per tile
 constexpr float kStale = 8.0f;   // base-2 headroom before the softmax reference moves
 
@@ -70,15 +69,20 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-template <int D>
-__global__ void __launch_bounds__(256, 2) ring_attn_step_kernel(AttnArgs a) {
+// W waves of 32 queries each share every staged K/V tile (W * 32 queries
+// per workgroup); two waves per SIMD either way (4 waves: two workgroups per
+// CU, 8 waves: one).
+template <int D, int W>
+__global__ void __launch_bounds__(64 * W, W == 4 ? 2 : 1) ring_attn_step_kernel(AttnArgs a) {
+    constexpr int NT = 64 * W;          // threads
+    constexpr int QT = 32 * W;          // queries per workgroup
     constexpr int KS = D / 16;          // k-steps of S^T = K Q^T
     constexpr int DB = D / 32;          // 32-row blocks of O^T
     constexpr int KP = D + 8;           // K tile pitch (elements)
     constexpr int VP = kKT + 8;         // transposed V tile pitch
     constexpr int CH = kKT * D / 8;     // 16-byte chunks per K (or V) tile
-    constexpr int CPT = CH / 256;       // chunks per thread
-    static_assert(CH % 256 == 0, "tile chunks must split evenly over the workgroup");
+    constexpr int CPT = CH / NT;        // chunks per thread
+    static_assert(CH % NT == 0, "tile chunks must split evenly over the workgroup");
     // Two buffers of (K tile [key][d], V tile transposed [d][key]): the next
     // tile is staged into one while the other is read, one barrier a tile.
     extern __shared__ __attribute__((aligned(16))) __bf16 lds[];
@@ -91,7 +95,7 @@ __global__ void __launch_bounds__(256, 2) ring_attn_step_kernel(AttnArgs a) {
     const int blk = a.fused ? (a.rank - step % a.t + a.t) % a.t : 0;
     const int64_t tok = a.b * a.heads * D;                     // elements per token
     const int64_t head_off = ((int64_t)bi * a.heads + hh) * D;
-    const int64_t qrow = (int64_t)blockIdx.x * kQT + wave * 32 + c;
+    const int64_t qrow = (int64_t)blockIdx.x * QT + wave * 32 + c;
     const int64_t qr = qrow < a.s_local ? qrow : a.s_local - 1;
 
     // Q^T operand: lane holds query c, d = 16*s + 8*g + 0..7.
@@ -107,19 +111,19 @@ __global__ void __launch_bounds__(256, 2) ring_attn_step_kernel(AttnArgs a) {
     const __bf16* vb = a.v + (int64_t)blk * a.s_local * tok + head_off;
 
     // The next tile's K and V travel in registers while this tile is
-    // computed.  K: chunk cc = tid + 256*i is key cc / (D/8), d = 8*(cc % (D/8)).
+    // computed.  K: chunk cc = tid + NT*i is key cc / (D/8), d = 8*(cc % (D/8)).
     // V: a thread owns one 8-wide d chunk of R consecutive keys, so its
     // transposed store is eight R-key runs (one 2R-byte write each).
     constexpr int R = CPT >= 4 ? 4 : CPT;
-    static_assert(CPT % R == 0 && (R == 2 || R == 4), "V is staged in runs of 2 or 4 keys");
+    static_assert(CPT % R == 0 && (R == 1 || R == 2 || R == 4), "V is staged in runs of 1, 2 or 4 keys");
     uint4 kn[CPT], vn[CPT];
     // Per-thread byte offsets inside a tile (the tile's base is uniform).
     uint32_t koff[CPT], voff[CPT];
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-        const int cc = tid + 256 * i, key = cc / (D / 8), dc = cc % (D / 8);
+        const int cc = tid + NT * i, key = cc / (D / 8), dc = cc % (D / 8);
         koff[i] = (uint32_t)(key * tok + 8 * dc) * 2u;
-        const int u = tid + 256 * (i / R), vdc = u % (D / 8), vkey = R * (u / (D / 8)) + (i % R);
+        const int u = tid + NT * (i / R), vdc = u % (D / 8), vkey = R * (u / (D / 8)) + (i % R);
         voff[i] = (uint32_t)(vkey * tok + 8 * vdc) * 2u;
     }
     auto fetch = [&](int64_t k0) {
@@ -134,10 +138,10 @@ __global__ void __launch_bounds__(256, 2) ring_attn_step_kernel(AttnArgs a) {
         } else {                                     // the ragged last tile: clamp
 #pragma unroll
             for (int i = 0; i < CPT; ++i) {
-                const int cc = tid + 256 * i, key = cc / (D / 8), dc = cc % (D / 8);
+                const int cc = tid + NT * i, key = cc / (D / 8), dc = cc % (D / 8);
                 const int64_t kk = k0 + key < a.s_local ? k0 + key : a.s_local - 1;
                 kn[i] = load_stream(kb + kk * tok + 8 * dc);
-                const int u = tid + 256 * (i / R), vdc = u % (D / 8);
+                const int u = tid + NT * (i / R), vdc = u % (D / 8);
                 const int vkey = R * (u / (D / 8)) + (i % R);
                 const int64_t vk = k0 + vkey < a.s_local ? k0 + vkey : a.s_local - 1;
                 vn[i] = load_stream(vb + vk * tok + 8 * vdc);
@@ -149,12 +153,12 @@ __global__ void __launch_bounds__(256, 2) ring_attn_step_kernel(AttnArgs a) {
         __bf16* vt = ks + KSZ;
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
-            const int cc = tid + 256 * i, key = cc / (D / 8), dc = cc % (D / 8);
+            const int cc = tid + NT * i, key = cc / (D / 8), dc = cc % (D / 8);
             *reinterpret_cast<uint4*>(&ks[key * KP + 8 * dc]) = kn[i];
         }
 #pragma unroll
         for (int iu = 0; iu < CPT / R; ++iu) {
-            const int u = tid + 256 * iu, vdc = u % (D / 8), vkey = R * (u / (D / 8));
+            const int u = tid + NT * iu, vdc = u % (D / 8), vkey = R * (u / (D / 8));
             bf16x8 v8[R];
 #pragma unroll
             for (int j = 0; j < R; ++j) v8[j] = __builtin_bit_cast(bf16x8, vn[R * iu + j]);
@@ -165,9 +169,11 @@ __global__ void __launch_bounds__(256, 2) ring_attn_step_kernel(AttnArgs a) {
                 if constexpr (R == 4) {
                     const bf16x4 run = {v8[0][e], v8[1][e], v8[2][e], v8[3][e]};
                     *reinterpret_cast<bf16x4*>(vrow + e * VP) = run;
-                } else {
+                } else if constexpr (R == 2) {
                     const bf16x2 run = {v8[0][e], v8[1][e]};
                     *reinterpret_cast<bf16x2*>(vrow + e * VP) = run;
+                } else {
+                    vrow[e * VP] = v8[0][e];
                 }
             }
         }
@@ -322,9 +328,9 @@ __global__ void __launch_bounds__(256) ring_attn_merge_kernel(AttnArgs a) {
     if (d0 == 0 && a.lse_out) a.lse_out[row] = lse;
 }
 
-template <int D>
-static hipError_t launch_attn(const AttnArgs& a, int steps, bool merge, hipStream_t s) {
-    const dim3 g((unsigned)((a.s_local + kQT - 1) / kQT), (unsigned)(a.b * a.heads),
+template <int D, int W>
+static hipError_t launch_step(const AttnArgs& a, int steps, hipStream_t s) {
+    const dim3 g((unsigned)((a.s_local + 32 * W - 1) / (32 * W)), (unsigned)(a.b * a.heads),
                  (unsigned)steps);
     constexpr size_t lds = 2 * ((size_t)kKT * (D + 8) + (size_t)D * (kKT + 8)) * sizeof(__bf16);
     // The dynamic LDS allowance is set once per device (bit d of `done`).
@@ -334,13 +340,20 @@ static hipError_t launch_attn(const AttnArgs& a, int steps, bool merge, hipStrea
     if (e != hipSuccess) return e;
     const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
     if (!bit || !(done.load(std::memory_order_acquire) & bit)) {
-        e = hipFuncSetAttribute((const void*)ring_attn_step_kernel<D>,
+        e = hipFuncSetAttribute((const void*)ring_attn_step_kernel<D, W>,
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         done.fetch_or(bit, std::memory_order_release);
     }
-    hipLaunchKernelGGL(ring_attn_step_kernel<D>, g, dim3(256), lds, s, a);
-    e = hipGetLastError();
+    hipLaunchKernelGGL((ring_attn_step_kernel<D, W>), g, dim3(64 * W), lds, s, a);
+    return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_attn(const AttnArgs& a, int steps, bool merge, hipStream_t s) {
+    // Eight waves: each staged tile serves 256 queries (the staging registers
+    // and the L2 -> LDS traffic per query halve against four waves).
+    hipError_t e = launch_step<D, 8>(a, steps, s);
     if (e != hipSuccess || !merge) return e;
     const int64_t nrows = a.s_local * a.b * a.heads;
     const int64_t rpb = 256 / (D / 4);
