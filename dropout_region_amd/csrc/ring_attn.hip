@@ -59,11 +59,18 @@ struct AttnArgs {
 constexpr int kKT = 64;    // keys per tile
 constexpr float kStale = 8.0f;   // base-2 headroom before the softmax reference moves
 
-// Column swizzle of the transposed V tile: key k of row d is stored at
-// column k ^ vswz(d).  Rows 8 apart (the rows one staging instruction's lanes
-// write) would otherwise fall in the same LDS bank; the XOR is a multiple of
-// 4 keys, so the 4-key runs that are written and read stay contiguous.
-__device__ __forceinline__ int vswz(int row) { return 4 * ((row >> 3) & 15); }
+// The transposed V tile [d][column] stores key vpos(j) in column j: bits 2
+// and 3 of the key index are swapped (the map is its own inverse).  The eight
+// keys one lane feeds into an O^T product, {4g..4g+3, 8+4g..8+4g+3} of a
+// 16-key group, then sit in eight adjacent columns: one 16-byte read.
+__device__ __forceinline__ constexpr int vpos(int key) {
+    return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
+}
+// Column swizzle: row d keeps its columns XOR-ed with vswz(d), a multiple of
+// 8 (the 16-byte read groups stay whole).  It spreads the 16 rows that one
+// staging write's lanes fill, and the rows 32 reading lanes cover, over
+// distinct LDS banks.
+__device__ __forceinline__ int vswz(int row) { return 8 * ((row >> 4) & 7); }
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -112,8 +119,10 @@ __global__ void __launch_bounds__(64 * W, W == 4 ? 2 : 1) ring_attn_step_kernel(
 
     // The next tile's K and V travel in registers while this tile is
     // computed.  K: chunk cc = tid + NT*i is key cc / (D/8), d = 8*(cc % (D/8)).
-    // V: a thread owns one 8-wide d chunk of R consecutive keys, so its
-    // transposed store is eight R-key runs (one 2R-byte write each).
+    // V: unit u = tid + NT*iu owns the 8-wide d chunk vdc = u % (D/8) of the R
+    // columns R*q .. R*q+R-1, q = u / (D/8), which hold the consecutive keys
+    // vpos(R*q) + 0..R-1; its transposed store is eight R-column runs (one
+    // 2R-byte write each).
     constexpr int R = CPT >= 4 ? 4 : CPT;
     static_assert(CPT % R == 0 && (R == 1 || R == 2 || R == 4), "V is staged in runs of 1, 2 or 4 keys");
     uint4 kn[CPT], vn[CPT];
@@ -123,7 +132,7 @@ __global__ void __launch_bounds__(64 * W, W == 4 ? 2 : 1) ring_attn_step_kernel(
     for (int i = 0; i < CPT; ++i) {
         const int cc = tid + NT * i, key = cc / (D / 8), dc = cc % (D / 8);
         koff[i] = (uint32_t)(key * tok + 8 * dc) * 2u;
-        const int u = tid + NT * (i / R), vdc = u % (D / 8), vkey = R * (u / (D / 8)) + (i % R);
+        const int u = tid + NT * (i / R), vdc = u % (D / 8), vkey = vpos(R * (u / (D / 8))) + (i % R);
         voff[i] = (uint32_t)(vkey * tok + 8 * vdc) * 2u;
     }
     auto fetch = [&](int64_t k0) {
@@ -142,7 +151,7 @@ __global__ void __launch_bounds__(64 * W, W == 4 ? 2 : 1) ring_attn_step_kernel(
                 const int64_t kk = k0 + key < a.s_local ? k0 + key : a.s_local - 1;
                 kn[i] = load_stream(kb + kk * tok + 8 * dc);
                 const int u = tid + NT * (i / R), vdc = u % (D / 8);
-                const int vkey = R * (u / (D / 8)) + (i % R);
+                const int vkey = vpos(R * (u / (D / 8))) + (i % R);
                 const int64_t vk = k0 + vkey < a.s_local ? k0 + vkey : a.s_local - 1;
                 vn[i] = load_stream(vb + vk * tok + 8 * vdc);
             }
@@ -158,12 +167,12 @@ __global__ void __launch_bounds__(64 * W, W == 4 ? 2 : 1) ring_attn_step_kernel(
         }
 #pragma unroll
         for (int iu = 0; iu < CPT / R; ++iu) {
-            const int u = tid + NT * iu, vdc = u % (D / 8), vkey = R * (u / (D / 8));
+            const int u = tid + NT * iu, vdc = u % (D / 8), col = R * (u / (D / 8));
             bf16x8 v8[R];
 #pragma unroll
             for (int j = 0; j < R; ++j) v8[j] = __builtin_bit_cast(bf16x8, vn[R * iu + j]);
-            // rows 8*vdc + e share vswz (= 4*(vdc % 16)): one column for all e
-            __bf16* vrow = &vt[8 * vdc * VP + (vkey ^ vswz(8 * vdc))];
+            // rows 8*vdc + e share vswz (= 8*((vdc/2) % 8)): one column for all e
+            __bf16* vrow = &vt[8 * vdc * VP + (col ^ vswz(8 * vdc))];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 if constexpr (R == 4) {
@@ -186,7 +195,8 @@ __global__ void __launch_bounds__(64 * W, W == 4 ? 2 : 1) ring_attn_step_kernel(
         for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
     float m = -INFINITY, l = 0.0f;      // running max (base-2 units) and sum of this query
 
-    const int vcol = (4 * g) ^ (4 * (c >> 3));     // lane part of the V^T read column
+    // Lane part of the V^T read column (see the O^T product below).
+    const int vcol = 8 * (g ^ (c >> 4));
     fetch(0);
     stage(0);
     __syncthreads();
@@ -203,13 +213,19 @@ __global__ void __launch_bounds__(64 * W, W == 4 ? 2 : 1) ring_attn_step_kernel(
         for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) st[cb][r] = 0.0f;
+        // Every K fragment is read before the first product (the reads
+        // return in order, so each product waits for its own fragment only).
+        bf16x8 kf[KS][2];
 #pragma unroll
         for (int s = 0; s < KS; ++s)
 #pragma unroll
-            for (int cb = 0; cb < 2; ++cb) {
-                const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&ks[(32 * cb + c) * KP + 16 * s + 8 * g]);
-                st[cb] = mfma32(ka, qv[s], st[cb]);
-            }
+            for (int cb = 0; cb < 2; ++cb)
+                kf[s][cb] = *reinterpret_cast<const bf16x8*>(&ks[(32 * cb + c) * KP + 16 * s + 8 * g]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) st[cb] = mfma32(kf[s][cb], qv[s], st[cb]);
         // Register r of block cb holds key 32*cb + 8*(r/4) + 4*g + r%4.  The
         // max is taken on the raw scores (the scale is positive) and the
         // scale enters through the exponent's FMA: p = 2^(s*c - m).
@@ -258,23 +274,24 @@ __global__ void __launch_bounds__(64 * W, W == 4 ? 2 : 1) ring_attn_step_kernel(
         l += psum;
         m = m_new;
 
-        // O^T += V^T P^T.  Product kg covers keys 32*(kg/2) + 16*(kg%2) + {4g..4g+3,
-        // 8+4g..8+4g+3} for lane group g: the keys its P^T operand holds.
-        // (kbase ^ vswz(row)) with kbase = 32*(kg/2) + 16*(kg%2) + 4*g and
-        // row = 32*db + c splits into a lane part in bits 2-3, 4*g ^ 4*(c/8),
-        // and a part in bits 4-5 known at compile time; kbase + 8 flips bit 3.
+        // O^T += V^T P^T.  Product kg covers keys kb + {4g..4g+3, 8+4g..8+4g+3},
+        // kb = 32*(kg/2) + 16*(kg%2): the keys its P^T operand holds, columns
+        // kb + 8g .. kb + 8g + 7 of row d = 32*db + c.  With vswz(d) =
+        // 16*(db%4) + 8*(c/16) the column splits into a compile-time part in
+        // bits 4-5, kb ^ 16*(db%4), and the lane part 8*(g ^ c/16) in bit 3.
+        bf16x8 vf[4][DB];
 #pragma unroll
-        for (int kg = 0; kg < 4; ++kg) {
+        for (int kg = 0; kg < 4; ++kg)
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
                 const int ct = (32 * (kg >> 1) + 16 * (kg & 1)) ^ (16 * (db & 3));
-                const __bf16* vr = vlane + 32 * db * VP + ct;
-                const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vr + vcol);
-                const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vr + (vcol ^ 8));
-                const bf16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                o[db] = mfma32(va, pb[kg], o[db]);
+                vf[kg][db] = *reinterpret_cast<const bf16x8*>(vlane + 32 * db * VP + ct + vcol);
             }
-        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kg = 0; kg < 4; ++kg)
+#pragma unroll
+            for (int db = 0; db < DB; ++db) o[db] = mfma32(vf[kg][db], pb[kg], o[db]);
         if (k0 + kKT < a.s_local) stage(cur ^ 1);   // the next tile, fetched a tile ago
         __syncthreads();            // staged tile visible; every wave is done with `cur`
         if (k0 + 2 * kKT < a.s_local) fetch(k0 + 2 * kKT);
