@@ -51,12 +51,13 @@ struct AttnArgs {
     float* lse_out;        // [s_local][b][heads]
     int64_t s_local, b;
     int heads, t, rank;
-    int step0;             // ring step of blockIdx.z == 0
+    int step0;             // ring step of the first step in the grid
     int fused;             // 1: k/v hold all t blocks, block (rank - step) mod t is used
     float scale_log2;      // softmax scale * log2(e): scores in base-2 units
 };
 
 constexpr int kKT = 64;    // keys per tile
+constexpr int kWaves = 8;  // waves per workgroup: 32 queries each
 constexpr float kStale = 8.0f;   // base-2 headroom before the softmax reference moves
 
 // The transposed V tile [d][column] stores key vpos(j) in column j: bits 2
@@ -97,12 +98,20 @@ __global__ void __launch_bounds__(64 * W, W == 4 ? 2 : 1) ring_attn_step_kernel(
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 5, c = lane & 31;
-    const int bi = (int)(blockIdx.y / a.heads), hh = (int)(blockIdx.y % a.heads);
-    const int step = a.step0 + (int)blockIdx.z;
+    // Workgroups go to the eight XCDs in turn (workgroup i to XCD i % 8), each
+    // with its own L2.  Renumbered so that consecutive logical tiles, the
+    // query tiles that stream the same K/V block, share an XCD and its L2.
+    const uint32_t total = gridDim.x, lin = blockIdx.x;
+    const uint32_t per = total / 8, rem = total % 8, xcd = lin % 8, slot = lin / 8;
+    const uint32_t logical = xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
+    const uint32_t nq = (uint32_t)((a.s_local + QT - 1) / QT), nbh = (uint32_t)(a.b * a.heads);
+    const uint32_t qtile = logical % nq, bh = (logical / nq) % nbh, sz = logical / nq / nbh;
+    const int bi = (int)(bh / a.heads), hh = (int)(bh % a.heads);
+    const int step = a.step0 + (int)sz;
     const int blk = a.fused ? (a.rank - step % a.t + a.t) % a.t : 0;
     const int64_t tok = a.b * a.heads * D;                     // elements per token
     const int64_t head_off = ((int64_t)bi * a.heads + hh) * D;
-    const int64_t qrow = (int64_t)blockIdx.x * QT + wave * 32 + c;
+    const int64_t qrow = (int64_t)qtile * QT + wave * 32 + c;
     const int64_t qr = qrow < a.s_local ? qrow : a.s_local - 1;
 
     // Q^T operand: lane holds query c, d = 16*s + 8*g + 0..7.
@@ -347,8 +356,9 @@ __global__ void __launch_bounds__(256) ring_attn_merge_kernel(AttnArgs a) {
 
 template <int D, int W>
 static hipError_t launch_step(const AttnArgs& a, int steps, hipStream_t s) {
-    const dim3 g((unsigned)((a.s_local + 32 * W - 1) / (32 * W)), (unsigned)(a.b * a.heads),
-                 (unsigned)steps);
+    // One grid dimension: query tiles x (batch, head) x steps, at most 2^31 - 1
+    // (the descriptor checks bound it).
+    const dim3 g((unsigned)((a.s_local + 32 * W - 1) / (32 * W) * a.b * a.heads * steps));
     constexpr size_t lds = 2 * ((size_t)kKT * (D + 8) + (size_t)D * (kKT + 8)) * sizeof(__bf16);
     // The dynamic LDS allowance is set once per device (bit d of `done`).
     static std::atomic<uint64_t> done{0};
@@ -370,7 +380,7 @@ template <int D>
 static hipError_t launch_attn(const AttnArgs& a, int steps, bool merge, hipStream_t s) {
     // Eight waves: each staged tile serves 256 queries (the staging registers
     // and the L2 -> LDS traffic per query halve against four waves).
-    hipError_t e = launch_step<D, 8>(a, steps, s);
+    hipError_t e = launch_step<D, kWaves>(a, steps, s);
     if (e != hipSuccess || !merge) return e;
     const int64_t nrows = a.s_local * a.b * a.heads;
     const int64_t rpb = 256 / (D / 4);
@@ -402,6 +412,9 @@ bool attn_desc_ok(const spr_attn_desc* d) {
     if (!(d->scale >= 0.0f) || isinf(d->scale)) return false;               // also NaN
     // every index (t blocks of s_local*b*heads*d elements) well inside 63 bits
     if ((double)d->t * (double)d->s_local * (double)d->b * d->heads * d->d > 4.0e18) return false;
+    // all steps' query tiles in one launch dimension
+    const int64_t qtiles = (d->s_local + 32 * kWaves - 1) / (32 * kWaves);
+    if ((double)qtiles * (double)d->b * d->heads * d->t > 2147483647.0) return false;
     return true;
 }
 

@@ -52,6 +52,8 @@ typedef struct {
     int32_t rank;      /* this rank, 0 <= rank < t: owns query block `rank`      */
     float   scale;     /* softmax scale; 0 means 1/sqrt(d)                       */
 } spr_attn_desc;
+/* Also rejected (SPR_ERR_INVALID_ARG): ceil(s_local/256) * b * heads * t above
+ * 2^31 - 1 (the 256-query tiles of all steps form one launch). */
 
 /* Bytes of workspace for the t partial results: fp32 O_k [t][s_local][b]
  * [heads][d] and L_k [t][s_local][b][heads].  0 on an invalid desc. */
