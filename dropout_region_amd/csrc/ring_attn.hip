@@ -9,11 +9,12 @@
 // tile of scores ("Sequence parallel math", section "Context parallelism and
 // ring attention").  No causal mask: every query sees every key.
 //
-// Kernel 1 (step): one workgroup per (128-query tile, batch x head, ring
-// step); at step k the block in hand is block (rank - k) mod t.  It walks
-// that block's keys in tiles of 64 with an online softmax and writes the
-// step's partial result: O_k normalised by its own sum, and its
-// log-sum-exp.  Kernel 2 (merge): per query and head, folds the partials in
+// Kernel 1 (step): one workgroup of eight waves per (256-query tile,
+// batch x head, ring step), on a one-dimensional grid ordered so that the
+// tiles streaming one K/V block share an XCD; at step k the block in hand is
+// block (rank - k) mod t.  It walks that block's keys in tiles of 64 with an
+// online softmax and writes the step's partial result: O_k normalised by its
+// own sum, and its log-sum-exp.  Kernel 2 (merge): per query and head, folds the partials in
 // ring order, acc = merge(acc, partial_k) for k = 0 .. t-1 -- the
 // accumulation a ring performs as the blocks arrive.
 //
