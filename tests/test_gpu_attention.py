@@ -100,3 +100,25 @@ def test_rank_changes_only_the_order():
         d = spr.AttnDesc(rank=rank, **kw)
         o, lse = spr.ring_attn(d, _dev(x["q"]), _dev(x["k"]), _dev(x["v"]))
         check_attention(f"rank {rank}", P.to_host(o), P.to_host(lse), want_o, want_lse, x["v"])
+
+
+@pytest.mark.parametrize("name", ["ring_attn_s32k_t8_h8192", "ring_attn_s2k_t8_d128"])
+def test_full_size_workload_sampled(name):
+    """The benchmark's workloads at their real shapes, in the launch the
+    benchmark times (every ring step in one call, then the merge); the oracle
+    computes a sample of query tokens -- first, last, and a few between --
+    over all keys and every (batch, head) pair."""
+    from sp_inputs import ATTN_WORKLOADS
+    w = ATTN_WORKLOADS[name]
+    kw = dict(s_local=w.s_local, b=w.b, heads=w.heads, d=w.d, t=w.t, rank=0)
+    _say(f"[case] ring attention full size {name}: {kw}")
+    x = make_attn_inputs(w.s_local, w.b, w.heads, w.d, w.t, seed=w.seed)
+    o, lse = spr.ring_attn(spr.AttnDesc(**kw), _dev(x["q"]), _dev(x["k"]), _dev(x["v"]))
+    go, gl = P.to_host(o), P.to_host(lse)
+    od = oracle.AttnDesc(**kw)
+    tok, nbh = w.b * w.heads * w.d, w.b * w.heads
+    for r in sorted({0, 1, w.s_local // 3, w.s_local // 2 + 7, w.s_local - 2, w.s_local - 1}):
+        want_o, want_lse = oracle.attention(od, x["q"][r * tok:(r + 1) * tok], x["k"], x["v"],
+                                            rows=(r, r + 1))
+        check_attention(f"{name} query {r}", go[r * tok:(r + 1) * tok],
+                        gl[r * nbh:(r + 1) * nbh], want_o, want_lse, x["v"])
