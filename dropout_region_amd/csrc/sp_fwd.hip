@@ -496,24 +496,17 @@ static hipError_t fwd_stream_by_norm(const spr_desc& d, const RowPlan& p, const 
                                    : fwd_stream_by_mode<IO, SPR_RMSNORM>(d, p, a, s);
 }
 
-// The stream kernel where its plan exists (at most 16 elements per thread,
-// so bias, gamma and beta fit in registers next to two row buffers) and the
-// shard has more than four rows per CU; else the row kernel.  Measured on
-// MI355X: with up to four rows per CU every row's workgroup is resident at
-// once and the row kernel is faster; with more, the stream kernel's overlap
-// of the next row's loads with the current row's work wins.
-// SPR_FWD_PATH=rows|stream asks for one kernel (tests check both).
+// The row kernel by default.  The stream kernel (where its plan exists: at
+// most 16 elements per thread, so bias, gamma and beta fit in registers next
+// to two row buffers) runs when SPR_FWD_PATH=stream asks for it; measured on
+// MI355X it is no faster anywhere the row kernel takes its preferred split
+// (long-sequence shard [4096, 1, 8192]: row kernel 59.2 us against 60.7 at
+// p = 0.1, 51.1 against 53.8 at p = 0).  SPR_FWD_PATH=rows|stream asks for
+// one kernel (tests check both).
 hipError_t launch_fwd(const spr_desc& d, const RowPlan& p, const FwdArgs& a, hipStream_t s) {
     RowPlan sp;
     const char* force = getenv("SPR_FWD_PATH");
-    bool stream = make_stream_plan(d.io, d.h, &sp);
-    if (stream && !(force && strcmp(force, "stream") == 0)) {
-        int cus = 0;
-        const hipError_t e = cu_count(&cus);
-        if (e != hipSuccess) return e;
-        stream = a.rows > 4 * (int64_t)cus;
-    }
-    if (force && strcmp(force, "rows") == 0) stream = false;
+    bool stream = force && strcmp(force, "stream") == 0 && make_stream_plan(d.io, d.h, &sp);
     if (a.nparts > 1) stream = false;    // the prologue is in the row kernel only
     if (stream)
         return d.io == SPR_BF16 ? fwd_stream_by_norm<__bf16>(d, sp, a, s)
