@@ -49,7 +49,9 @@ constexpr int bwd_depth(int vpt, int lb, bool wave_rows, bool layernorm) {
                      : (vpt == 1 ? ((lb <= 768 || !layernorm) ? 3 : 2) : 1);
 }
 
-enum PlanKind { kPlanForward, kPlanBackward };
+// Forward, the forward's norm-only entry (x absent: residual in, y out), or
+// the backward: each has its own preference of vectors per thread.
+enum PlanKind { kPlanForward, kPlanEntry, kPlanBackward };
 
 // How the backward learns the dropout decisions: none (p == 0), from the
 // stored mask, or regenerated from the counter-based generator (the forward

@@ -32,18 +32,22 @@ bool make_row_plan(int io, int64_t h, PlanKind kind, RowPlan* plan) {
     // whose split leaves no vector slot idle, else the one wasting fewest.
     // The forward prefers more vectors per thread: more loads in flight per
     // thread and a smaller reduction (measured on MI355X, 22B shard: 6
-    // vectors per thread 14.8 us, 4: 16.0, 3: 15.5, 2: 17.3).
+    // vectors per thread 14.8 us, 4: 16.0, 3: 15.5, 2: 17.3).  The norm-only
+    // entry, which loads half as much per element, is fastest at 4 (22B
+    // shard: 8.0 us against 12.3 at 6).
     static const int kFwdOrder[] = {6, 4, 3, 5, 2, 8, 1};
+    static const int kEntryOrder[] = {4, 3, 5, 6, 2, 8, 1};
     static const int kBwdOrder[] = {1, 2, 3, 4, 5, 6, 8};
-    const int* order = (kind == kPlanForward) ? kFwdOrder : kBwdOrder;
+    const bool fwd = kind != kPlanBackward;
+    const int* order = kind == kPlanForward ? kFwdOrder : (kind == kPlanEntry ? kEntryOrder : kBwdOrder);
     int best_vpt = 0, best_lb = 0;
     int64_t best_tpr = 0, best_waste = INT64_MAX;
     for (int i = 0; i < 7; ++i) {
         const int v = order[i];
         const int64_t tpr = ((nvec + v - 1) / v + 63) / 64 * 64;
-        const VptBound* tab = (kind == kPlanForward) ? kWgCombos : kBwdCombos;
-        const int ntab = (kind == kPlanForward) ? (int)(sizeof kWgCombos / sizeof kWgCombos[0])
-                                                : (int)(sizeof kBwdCombos / sizeof kBwdCombos[0]);
+        const VptBound* tab = fwd ? kWgCombos : kBwdCombos;
+        const int ntab = fwd ? (int)(sizeof kWgCombos / sizeof kWgCombos[0])
+                             : (int)(sizeof kBwdCombos / sizeof kBwdCombos[0]);
         int lb = 0;                          // the smallest compiled bound that fits
         for (int t = 0; t < ntab; ++t)
             if (tab[t].vpt == v && tab[t].lb >= tpr && (lb == 0 || tab[t].lb < lb)) lb = tab[t].lb;
@@ -197,7 +201,7 @@ spr_status fwd_impl(const spr_desc* d, const void* x, int nparts, const float* b
                     void* y_out, uint8_t* mask_out, float* mean_out, float* rstd_out,
                     hipStream_t stream) {
     RowPlan plan;
-    spr_status st = check_desc(d, &plan, kPlanForward);
+    spr_status st = check_desc(d, &plan, x ? kPlanForward : kPlanEntry);
     if (st != SPR_OK) return st;
     const bool ln = d->norm == SPR_LAYERNORM, drop = d->p > 0.0f;
     if (!residual || (!x && !gamma)) return SPR_ERR_INVALID_ARG;
