@@ -376,3 +376,45 @@ def bwd(d, dy, dh_out, h, mask, mean, rstd, gamma, want_dbias=True, stream=None)
     sp_region_bwd(d, dy, dh_out, h, mask, mean, rstd, gamma, o["dx"], o["dres"], o["dgamma"],
                   o["dbeta"], o["dbias"], o["workspace"], stream)
     return o
+
+
+def _region_function():
+    import torch
+
+    class SPRegionFunction(torch.autograd.Function):
+        """The region as an autograd function on one shard: (y, h) =
+        region(x, residual, bias, gamma, beta).  Inputs are flat [N*h]
+        tensors in the I/O type (bias, gamma, beta fp32 [h]; bias and beta
+        may be None).  Forward: sp_region_fwd with the mask stored; backward:
+        sp_region_bwd from the saved h, mask and statistics, with the gradient
+        reaching h from outside the region passed as dh_out."""
+
+        @staticmethod
+        def forward(ctx, x, residual, bias, gamma, beta, d):
+            o = fwd(d, x, bias, residual, gamma, beta)
+            ctx.save_for_backward(o["h"], o["mask"], o["mean"], o["rstd"], gamma)
+            ctx.d, ctx.want_dbias = d, bias is not None
+            return o["y"], o["h"]
+
+        @staticmethod
+        def backward(ctx, dy, dh):
+            h, mask, mean, rstd, gamma = ctx.saved_tensors
+            if dy is None:
+                dy = torch.zeros_like(h)
+            g = bwd(ctx.d, dy.contiguous(), None if dh is None else dh.contiguous(), h, mask,
+                    mean, rstd, gamma, want_dbias=ctx.want_dbias)
+            return g["dx"], g["dres"], g["dbias"], g["dgamma"], g["dbeta"], None
+
+    return SPRegionFunction
+
+
+def region(d, x, residual, bias, gamma, beta):
+    """(y, h) of the region on one shard, differentiable through
+    sp_region_bwd (see SPRegionFunction in _region_function)."""
+    global _REGION_FN
+    if _REGION_FN is None:
+        _REGION_FN = _region_function()
+    return _REGION_FN.apply(x, residual, bias, gamma, beta, d)
+
+
+_REGION_FN = None
