@@ -88,6 +88,8 @@ SMALL = {
     "bf16_ln_p0.9": base(s_local=4, b=2, h=6144, p=0.9),
     "fp32_ln_h8192_1100_rows": base(s_local=550, b=2, h=8192, io=F32),
     "bf16_rms_h12288_1500_rows": base(s_local=500, b=3, h=12288, norm=RMS, p=0.2),
+    # 378 vectors: six per thread over 64-thread teams, six slots idle (ragged)
+    "bf16_ln_h3024_ragged_six": base(s_local=9, b=2, h=3024),
 }
 
 
@@ -141,6 +143,7 @@ RS = {
     "bf16_rms_h8192_5_parts": (base(s_local=20, b=1, h=8192, norm=RMS, eps=1e-6), 5),
     "fp32_ln_h260_ragged_3_parts": (base(s_local=13, b=3, h=260, io=F32), 3),
     "bf16_ln_h25600_t2": (base(s_local=3, b=2, h=25600, shard_index=1, t=2), 2),
+    "bf16_ln_h3024_ragged_3_parts": (base(s_local=9, b=2, h=3024), 3),
     "bf16_ln_h32768_widest_9_parts": (base(s_local=2, b=1, h=32768), 9),
     "bf16_ln_h8192_1100_rows_t4": (base(s_local=1100, b=1, h=8192, t=4, shard_index=2), 4),
     "bf16_ln_h1000_wave_rows_p0_6_parts": (base(s_local=37, b=1, h=1000, p=0.0), 6),
@@ -174,6 +177,7 @@ ENTRY = {
     "bf16_ln_h1000_wave_rows": base(s_local=37, b=1, h=1000, p=0.0),
     "bf16_rms_h8192_1100_rows": base(s_local=1100, b=1, h=8192, norm=RMS, p=0.0, eps=1e-6),
     "bf16_ln_h25600": base(s_local=3, b=2, h=25600, p=0.0),
+    "bf16_ln_h3024_ragged": base(s_local=9, b=2, h=3024, p=0.0),
 }
 
 
@@ -223,6 +227,7 @@ EXIT = {
     "bf16_h25600_p0": base(s_local=3, b=2, h=25600, p=0.0),
     "bf16_h8192_1100_rows": base(s_local=1100, b=1, h=8192, offset=5),
     "fp32_h4_single_vector": base(s_local=9, b=1, h=4, io=F32, p=0.5),
+    "bf16_h3024_ragged_p0.1": base(s_local=9, b=2, h=3024),
 }
 
 
