@@ -10,13 +10,16 @@
 // ring attention").  No causal mask: every query sees every key.
 //
 // Kernel 1 (step): one workgroup of eight waves per (256-query tile,
-// batch x head, ring step), on a one-dimensional grid ordered so that the
-// tiles streaming one K/V block share an XCD; at step k the block in hand is
-// block (rank - k) mod t.  It walks that block's keys in tiles of 64 with an
-// online softmax and writes the step's partial result: O_k normalised by its
-// own sum, and its log-sum-exp.  Kernel 2 (merge): per query and head, folds the partials in
-// ring order, acc = merge(acc, partial_k) for k = 0 .. t-1 -- the
-// accumulation a ring performs as the blocks arrive.
+// batch x head, group of consecutive ring steps), on a one-dimensional grid
+// ordered so that the tiles streaming the same K/V blocks share an XCD; at
+// step k the block in hand is block (rank - k) mod t.  It walks the blocks of
+// its steps in ring order as one run of 64-key tiles with an online softmax
+// and writes the group's partial result: O normalised by its own sum, and its
+// log-sum-exp.  (One step per workgroup when the steps arrive one at a time;
+// the fused call groups them so that about one workgroup per CU remains.)
+// Kernel 2 (merge): per query and head, folds the partials in ring order,
+// acc = merge(acc, partial_k) -- the accumulation a ring performs as the
+// blocks arrive.
 //
 // Matrix products on MFMA (v_mfma_f32_32x32x16_bf16; bf16 operands, fp32
 // accumulation).  Each wave owns 32 queries and computes S^T = K Q^T, so a
@@ -30,6 +33,7 @@
 #include <math.h>
 
 #include <atomic>
+#include <cstdlib>
 
 #include "sp_device.h"
 #include "sp_host_checks.h"
@@ -52,8 +56,10 @@ struct AttnArgs {
     float* lse_out;        // [s_local][b][heads]
     int64_t s_local, b;
     int heads, t, rank;
-    int step0;             // ring step of the first step in the grid
+    int step0;             // ring step of the first step in the grid (one-step calls)
     int fused;             // 1: k/v hold all t blocks, block (rank - step) mod t is used
+    int spg;               // ring steps per workgroup, walked as one run of key tiles
+    int nparts;            // partial results the merge folds, in ring order
     float scale_log2;      // softmax scale * log2(e): scores in base-2 units
 };
 
@@ -81,7 +87,9 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 // W waves of 32 queries each share every staged K/V tile (W * 32 queries
 // per workgroup); two waves per SIMD either way (4 waves: two workgroups per
 // CU, 8 waves: one).
-template <int D, int W>
+// RUN: the workgroup walks a.spg > 1 ring steps as one run of key tiles;
+// without it, one step (a.spg == 1) and no block changes inside the loop.
+template <int D, int W, bool RUN>
 __global__ void __launch_bounds__(64 * W, W == 4 ? 2 : 1) ring_attn_step_kernel(AttnArgs a) {
     constexpr int NT = 64 * W;          // threads
     constexpr int QT = 32 * W;          // queries per workgroup
@@ -108,8 +116,9 @@ __global__ void __launch_bounds__(64 * W, W == 4 ? 2 : 1) ring_attn_step_kernel(
     const uint32_t nq = (uint32_t)((a.s_local + QT - 1) / QT), nbh = (uint32_t)(a.b * a.heads);
     const uint32_t qtile = logical % nq, bh = (logical / nq) % nbh, sz = logical / nq / nbh;
     const int bi = (int)(bh / a.heads), hh = (int)(bh % a.heads);
-    const int step = a.step0 + (int)sz;
-    const int blk = a.fused ? (a.rank - step % a.t + a.t) % a.t : 0;
+    // Workgroup group sz covers ring steps first .. first + spg - 1, one after
+    // another as one run of key tiles, and writes partial slot `part`.
+    const int part = a.step0 + (int)sz, first = a.step0 + (int)sz * a.spg;
     const int64_t tok = a.b * a.heads * D;                     // elements per token
     const int64_t head_off = ((int64_t)bi * a.heads + hh) * D;
     const int64_t qrow = (int64_t)qtile * QT + wave * 32 + c;
@@ -124,8 +133,16 @@ __global__ void __launch_bounds__(64 * W, W == 4 ? 2 : 1) ring_attn_step_kernel(
         qv[s] = __builtin_bit_cast(bf16x8, w);
     }
 
-    const __bf16* kb = a.k + (int64_t)blk * a.s_local * tok + head_off;
-    const __bf16* vb = a.v + (int64_t)blk * a.s_local * tok + head_off;
+    // The run: for each ring step first .. first + spg - 1, the key tiles
+    // k0 = 0, 64, ... of the block in hand at that step.  The fetch walks it one
+    // tile ahead of the staging (f_k0, f_step: the next tile to fetch).
+    const int64_t ntiles = (a.s_local + kKT - 1) / kKT * (RUN ? a.spg : 1);
+    auto block_off = [&](int step) {
+        const int blk = a.fused ? (a.rank - step % a.t + a.t) % a.t : 0;
+        return (int64_t)blk * a.s_local * tok + head_off;
+    };
+    int64_t f_k0 = 0, f_boff = block_off(first);
+    int f_step = first;
 
     // The next tile's K and V travel in registers while this tile is
     // computed.  K: chunk cc = tid + NT*i is key cc / (D/8), d = 8*(cc % (D/8)).
@@ -145,7 +162,17 @@ __global__ void __launch_bounds__(64 * W, W == 4 ? 2 : 1) ring_attn_step_kernel(
         const int u = tid + NT * (i / R), vdc = u % (D / 8), vkey = vpos(R * (u / (D / 8))) + (i % R);
         voff[i] = (uint32_t)(vkey * tok + 8 * vdc) * 2u;
     }
-    auto fetch = [&](int64_t k0) {
+    auto fetch = [&]() {
+        const int64_t k0 = f_k0;
+        const __bf16* kb = a.k + f_boff;
+        const __bf16* vb = a.v + f_boff;
+        f_k0 += kKT;                                 // advance the run
+        if constexpr (RUN) {
+            if (f_k0 >= a.s_local) {                 // into the next step's block
+                f_k0 = 0;
+                f_boff = block_off(++f_step);
+            }
+        }
         const char* kt = reinterpret_cast<const char*>(kb + k0 * tok);
         const char* vt0 = reinterpret_cast<const char*>(vb + k0 * tok);
         if (k0 + kKT <= a.s_local) {                 // a whole tile (uniform)
@@ -207,12 +234,13 @@ __global__ void __launch_bounds__(64 * W, W == 4 ? 2 : 1) ring_attn_step_kernel(
 
     // Lane part of the V^T read column (see the O^T product below).
     const int vcol = 8 * (g ^ (c >> 4));
-    fetch(0);
+    fetch();
     stage(0);
     __syncthreads();
-    if (kKT < a.s_local) fetch(kKT);
+    if (ntiles > 1) fetch();
     int cur = 0;
-    for (int64_t k0 = 0; k0 < a.s_local; k0 += kKT) {
+    int64_t k0 = 0;                     // keys of the current tile within its block
+    for (int64_t ti = 0; ti < ntiles; ++ti, k0 = (RUN && k0 + kKT >= a.s_local) ? 0 : k0 + kKT) {
         const __bf16* ks = lds + cur * BUF;
         const __bf16* vlane = ks + KSZ + c * VP;
 
@@ -302,15 +330,16 @@ __global__ void __launch_bounds__(64 * W, W == 4 ? 2 : 1) ring_attn_step_kernel(
         for (int kg = 0; kg < 4; ++kg)
 #pragma unroll
             for (int db = 0; db < DB; ++db) o[db] = mfma32(vf[kg][db], pb[kg], o[db]);
-        if (k0 + kKT < a.s_local) stage(cur ^ 1);   // the next tile, fetched a tile ago
+        if (ti + 1 < ntiles) stage(cur ^ 1);   // the next tile, fetched a tile ago
         __syncthreads();            // staged tile visible; every wave is done with `cur`
-        if (k0 + 2 * kKT < a.s_local) fetch(k0 + 2 * kKT);
+        if (ti + 2 < ntiles) fetch();
         cur ^= 1;
     }
 
-    // The step's partial: O / l and its log-sum-exp (natural log).
+    // The partial of the workgroup's steps: O / l and its log-sum-exp
+    // (natural log).
     if (qrow < a.s_local) {
-        const int64_t row = ((int64_t)step * a.s_local + qrow) * a.b * a.heads +
+        const int64_t row = ((int64_t)part * a.s_local + qrow) * a.b * a.heads +
                             (int64_t)bi * a.heads + hh;
         const float inv_l = 1.0f / l;
         float* po = a.part_o + row * D;
@@ -325,7 +354,7 @@ __global__ void __launch_bounds__(64 * W, W == 4 ? 2 : 1) ring_attn_step_kernel(
     }
 }
 
-// Merge: per (query, batch, head) row, the t partials in ring order.  A row
+// Merge: per (query, batch, head) row, the nparts partials in ring order.  A row
 // is D/4 threads, each owning 4 consecutive d; the folded result is written
 // as bf16 O and fp32 log-sum-exp.
 template <int D>
@@ -337,7 +366,7 @@ __global__ void __launch_bounds__(256) ring_attn_merge_kernel(AttnArgs a) {
     if (row >= nrows) return;
     float lse = a.part_lse[row];
     float4 o = *reinterpret_cast<const float4*>(a.part_o + row * D + d0);
-    for (int k = 1; k < a.t; ++k) {
+    for (int k = 1; k < a.nparts; ++k) {
         const int64_t pr = (int64_t)k * nrows + row;
         const float lk = a.part_lse[pr];
         const float4 ok = *reinterpret_cast<const float4*>(a.part_o + pr * D + d0);
@@ -355,10 +384,10 @@ __global__ void __launch_bounds__(256) ring_attn_merge_kernel(AttnArgs a) {
     if (d0 == 0 && a.lse_out) a.lse_out[row] = lse;
 }
 
-template <int D, int W>
+template <int D, int W, bool RUN>
 static hipError_t launch_step(const AttnArgs& a, int steps, hipStream_t s) {
-    // One grid dimension: query tiles x (batch, head) x steps, at most 2^31 - 1
-    // (the descriptor checks bound it).
+    // One grid dimension: query tiles x (batch, head) x groups of steps, at
+    // most 2^31 - 1 (the descriptor checks bound it).
     const dim3 g((unsigned)((a.s_local + 32 * W - 1) / (32 * W) * a.b * a.heads * steps));
     constexpr size_t lds = 2 * ((size_t)kKT * (D + 8) + (size_t)D * (kKT + 8)) * sizeof(__bf16);
     // The dynamic LDS allowance is set once per device (bit d of `done`).
@@ -368,12 +397,12 @@ static hipError_t launch_step(const AttnArgs& a, int steps, hipStream_t s) {
     if (e != hipSuccess) return e;
     const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
     if (!bit || !(done.load(std::memory_order_acquire) & bit)) {
-        e = hipFuncSetAttribute((const void*)ring_attn_step_kernel<D, W>,
+        e = hipFuncSetAttribute((const void*)ring_attn_step_kernel<D, W, RUN>,
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         done.fetch_or(bit, std::memory_order_release);
     }
-    hipLaunchKernelGGL((ring_attn_step_kernel<D, W>), g, dim3(64 * W), lds, s, a);
+    hipLaunchKernelGGL((ring_attn_step_kernel<D, W, RUN>), g, dim3(64 * W), lds, s, a);
     return hipGetLastError();
 }
 
@@ -381,7 +410,8 @@ template <int D>
 static hipError_t launch_attn(const AttnArgs& a, int steps, bool merge, hipStream_t s) {
     // Eight waves: each staged tile serves 256 queries (the staging registers
     // and the L2 -> LDS traffic per query halve against four waves).
-    hipError_t e = launch_step<D, kWaves>(a, steps, s);
+    hipError_t e = a.spg > 1 ? launch_step<D, kWaves, true>(a, steps, s)
+                             : launch_step<D, kWaves, false>(a, steps, s);
     if (e != hipSuccess || !merge) return e;
     const int64_t nrows = a.s_local * a.b * a.heads;
     const int64_t rpb = 256 / (D / 4);
@@ -429,6 +459,25 @@ uint64_t workspace_need(const spr_attn_desc* d) {
     return part_o_bytes(d) + (((uint64_t)d->t * rows_of(d) * 4u + 255u) & ~(uint64_t)255u);
 }
 
+// Ring steps per workgroup in the fused call: the largest divisor k of t
+// that still leaves at least 256 workgroups (one per CU), so each workgroup
+// walks a longer run of key tiles and the merge folds t / k partials instead
+// of t (measured on MI355X, 4096 queries x 32768 keys: 4 steps per workgroup
+// 529 us, 2: 544, 1: 557).  SPR_ATTN_STEPS_PER_WG=k asks for k (a divisor of
+// t; tests check several).
+int steps_per_workgroup(const spr_attn_desc* d) {
+    const char* env = getenv("SPR_ATTN_STEPS_PER_WG");
+    if (env) {
+        const int k = atoi(env);
+        if (k >= 1 && d->t % k == 0) return k;
+    }
+    const int64_t per_step = (d->s_local + 32 * kWaves - 1) / (32 * kWaves) * d->b * d->heads;
+    int spg = 1;
+    for (int k = 2; k <= d->t; ++k)
+        if (d->t % k == 0 && per_step * (d->t / k) >= 256) spg = k;
+    return spg;
+}
+
 AttnArgs make_args(const spr_attn_desc* d, void* workspace) {
     AttnArgs a{};
     a.part_o = static_cast<float*>(workspace);
@@ -438,6 +487,8 @@ AttnArgs make_args(const spr_attn_desc* d, void* workspace) {
     a.heads = d->heads;
     a.t = d->t;
     a.rank = d->rank;
+    a.spg = 1;
+    a.nparts = d->t;
     const double scale = d->scale > 0.0f ? (double)d->scale : 1.0 / sqrt((double)d->d);
     a.scale_log2 = (float)((double)(float)scale * 1.4426950408889634);
     return a;
@@ -519,7 +570,9 @@ spr_status sp_ring_attn_fwd(const spr_attn_desc* d, const void* q, const void* k
     a.lse_out = lse_out;
     a.step0 = 0;
     a.fused = 1;
-    return launch_ring_attn(d->d, a, d->t, true, stream) == hipSuccess ? SPR_OK : SPR_ERR_HIP;
+    a.spg = steps_per_workgroup(d);
+    a.nparts = d->t / a.spg;
+    return launch_ring_attn(d->d, a, a.nparts, true, stream) == hipSuccess ? SPR_OK : SPR_ERR_HIP;
 }
 
 }  // extern "C"

@@ -51,6 +51,7 @@ def check_attention(name, got_o, got_lse, want_o, want_lse, v_bits):
 
 
 CASES = {
+    "d128_t6_two_ragged_blocks": dict(s_local=70, b=1, heads=2, d=128, t=6, rank=4),
     "d128_full_tiles_t4_rank1": dict(s_local=256, b=1, heads=2, d=128, t=4, rank=1),
     "d64_ragged_b2_t3_rank2": dict(s_local=100, b=2, heads=3, d=64, t=3, rank=2),
     "d128_one_token_t1": dict(s_local=1, b=1, heads=1, d=128, t=1, rank=0),
@@ -62,13 +63,20 @@ CASES = {
 
 @pytest.mark.parametrize("name", sorted(CASES))
 def test_ring_attention_matches_oracle(name):
+    """Every case with the workgroups taking one ring step each, all t steps
+    each (one run of key tiles across the blocks, one partial), and the
+    launch's own choice."""
     kw = CASES[name]
     d, od = spr.AttnDesc(**kw), oracle.AttnDesc(**kw)
-    _say(f"[case] ring attention {name}: {kw}")
     x = make_attn_inputs(d.s_local, d.b, d.heads, d.d, d.t, seed=zlib.crc32(name.encode()) % 1000)
     want_o, want_lse = oracle.attention(od, x["q"], x["k"], x["v"])
-    o, lse = spr.ring_attn(d, _dev(x["q"]), _dev(x["k"]), _dev(x["v"]))
-    check_attention(name, P.to_host(o), P.to_host(lse), want_o, want_lse, x["v"])
+    mid = [str(k) for k in range(2, d.t) if d.t % k == 0][:1]   # a proper divisor, if any
+    for spg in sorted({None, "1", str(d.t), *mid}, key=str):
+        _say(f"[case] ring attention {name}: {kw}, steps per workgroup {spg}")
+        with P._env("SPR_ATTN_STEPS_PER_WG", spg):
+            o, lse = spr.ring_attn(d, _dev(x["q"]), _dev(x["k"]), _dev(x["v"]))
+        check_attention(f"{name} spg {spg}", P.to_host(o), P.to_host(lse), want_o, want_lse,
+                        x["v"])
 
 
 def test_steps_in_any_order_then_merge_equal_the_fused_call():
