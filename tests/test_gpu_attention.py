@@ -52,6 +52,7 @@ def check_attention(name, got_o, got_lse, want_o, want_lse, v_bits):
 
 CASES = {
     "d128_t6_two_ragged_blocks": dict(s_local=70, b=1, heads=2, d=128, t=6, rank=4),
+    "d64_one_token_t8_rank3": dict(s_local=1, b=2, heads=3, d=64, t=8, rank=3),
     "d128_full_tiles_t4_rank1": dict(s_local=256, b=1, heads=2, d=128, t=4, rank=1),
     "d64_ragged_b2_t3_rank2": dict(s_local=100, b=2, heads=3, d=64, t=3, rank=2),
     "d128_one_token_t1": dict(s_local=1, b=1, heads=1, d=128, t=1, rank=0),
