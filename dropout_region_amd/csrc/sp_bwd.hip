@@ -281,7 +281,16 @@ __global__ void __launch_bounds__(256) sp_region_bwd_finalize_kernel(BwdArgs a) 
 // w, w + 4, ... and prefetch the next group of U rows while computing the
 // current one; dx/dresidual are written and the dgamma/dbeta/dbias column
 // partials of the tile's rows are added across the waves in wave order.
-constexpr int kSplitWaves = 4, kSplitUnroll = 4;
+#ifndef SPR_SPLIT_U
+#define SPR_SPLIT_U 4
+#endif
+#ifndef SPR_SPLIT_PREFETCH
+#define SPR_SPLIT_PREFETCH 1
+#endif
+#ifndef SPR_EXIT_U
+#define SPR_EXIT_U 4
+#endif
+constexpr int kSplitWaves = 4, kSplitUnroll = SPR_SPLIT_U, kExitUnroll = SPR_EXIT_U;
 
 template <typename IO, int NORM, int VPT, bool WAVE_ROWS, int LB, bool EXACT>
 __global__ void __launch_bounds__(LB) sp_region_bwd_rowsum_kernel(BwdArgs a) {
@@ -416,13 +425,7 @@ __global__ void __launch_bounds__(256) sp_region_bwd_main_kernel(BwdArgs a) {
         }
     };
 
-    // Trip counts differ between waves (ragged tiles) but nothing in the loop
-    // synchronises the workgroup.
-    TileIn<U, MW> cur, nxt;
-    int64_t base = r0 + wave;
-    if (base < r1) load_group(base, cur);
-    for (; base < r1; base += step) {
-        if (base + step < r1) load_group(base + step, nxt);
+    auto process_group = [&](int64_t base, const TileIn<U, MW>& cur) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t row = base + kSplitWaves * u;
@@ -465,7 +468,25 @@ __global__ void __launch_bounds__(256) sp_region_bwd_main_kernel(BwdArgs a) {
                 if (a.dx_out) dx.store(static_cast<IO*>(a.dx_out) + off);
             }
         }
-        cur = nxt;
+    };
+
+    // Trip counts differ between waves (ragged tiles) but nothing in the loop
+    // synchronises the workgroup.
+    if constexpr (SPR_SPLIT_PREFETCH) {
+        TileIn<U, MW> cur, nxt;
+        int64_t base = r0 + wave;
+        if (base < r1) load_group(base, cur);
+        for (; base < r1; base += step) {
+            if (base + step < r1) load_group(base + step, nxt);
+            process_group(base, cur);
+            cur = nxt;
+        }
+    } else {
+        for (int64_t base = r0 + wave; base < r1; base += step) {
+            TileIn<U, MW> cur;
+            load_group(base, cur);
+            process_group(base, cur);
+        }
     }
     split_store_colpart<E>(a, sh, acc_g, 0, vec, ok);
     split_store_colpart<E>(a, sh, acc_b, 1, vec, ok);
@@ -489,7 +510,7 @@ struct ExitIn {
 template <typename IO, int DROP>
 __global__ void __launch_bounds__(256) sp_region_bwd_exit_kernel(BwdArgs a) {
     using V = Vec<IO>;
-    constexpr int E = V::N, U = kSplitUnroll, MW = E / 4;
+    constexpr int E = V::N, U = kExitUnroll, MW = E / 4;
     __shared__ float sh[kSplitWaves][64][E];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -558,7 +579,7 @@ __global__ void __launch_bounds__(256) sp_region_bwd_exit_kernel(BwdArgs a) {
 static hipError_t launch_finalize(const BwdArgs& a, hipStream_t s);
 
 hipError_t launch_bwd_exit(const spr_desc& d, const BwdPlan& p, const BwdArgs& a, hipStream_t s) {
-    const dim3 g((unsigned)p.col_tiles, (unsigned)p.row_blocks), b(256);
+    const dim3 g((unsigned)p.col_tiles, (unsigned)p.exit_row_blocks), b(256);
     const int mode = !(d.p > 0.0f) ? kDropNone : (a.mask ? kDropMask : kDropRegen);
     if (d.io == SPR_BF16) {
         if (mode == kDropMask)

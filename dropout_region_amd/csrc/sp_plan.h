@@ -143,8 +143,10 @@ struct BwdPlan {
     int col_tiles;         // split
     int tile_rows;         // split
     int64_t row_blocks;    // split: partial rows
+    int exit_tile_rows;    // norm-free exit: rows per tile
+    int64_t exit_row_blocks;  // norm-free exit: partial rows
     size_t rowpart_bytes;  // split: offset of the column partials in the workspace
-    size_t workspace;      // bytes either path needs (the larger of the two)
+    size_t workspace;      // bytes any of the three needs (the largest)
 };
 
 bool make_bwd_plan(const spr_desc& d, BwdPlan* plan);

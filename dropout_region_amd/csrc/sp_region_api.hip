@@ -134,19 +134,40 @@ bool make_bwd_plan(const spr_desc& d, BwdPlan* plan) {
     p.teams = bwd_teams(d, p.rows);
 
     p.col_tiles = (p.rows.nvec + 63) / 64;
-    // About one 4-wave tile per CU, rows per tile a multiple of 16.
-    int64_t tr = rows * p.col_tiles / 256;
-    tr = tr / 16 * 16;
-    if (tr < 16) tr = 16;
+    // Rows per tile, a multiple of the 16 rows a workgroup's four waves take
+    // per group: 32 for the split path's second pass, 16 for the exit.  Many
+    // small tiles keep several workgroups per CU loading at once, and the
+    // partial rows they add stay a few % of the bytes (3*h fp32 per tile row
+    // against 9 bytes per element in, 1*h against 5).  Measured on MI355X
+    // against about one tile per CU: split second pass + finalize 61.6 ->
+    // 47.7 us on the 175B shard, 358 -> 328 us on the 1T t = 1 shard; exit
+    // 33.4 -> 27.4 us (175B), 194 -> 176 us (1T t = 1).
+    // SPR_BWD_TILE_ROWS=n (a multiple of 16) overrides both.
     const int64_t rows16 = (rows + 15) / 16 * 16;
+    int64_t tr = 32, tr_exit = 16;
+    const char* trs = getenv("SPR_BWD_TILE_ROWS");
+    if (trs) {
+        const long v = strtol(trs, nullptr, 10);
+        if (v >= 16 && v % 16 == 0 && v <= (1L << 20)) tr = tr_exit = v;
+    }
+    // The row blocks are the grid's y dimension, at most 65535.
+    const int64_t min_tr = ((rows + 65534) / 65535 + 15) / 16 * 16;
+    if (tr < min_tr) tr = min_tr;
+    if (tr_exit < min_tr) tr_exit = min_tr;
     if (tr > rows16) tr = rows16;
+    if (tr_exit > rows16) tr_exit = rows16;
     p.tile_rows = (int)tr;
     p.row_blocks = (rows + tr - 1) / tr;
+    p.exit_tile_rows = (int)tr_exit;
+    p.exit_row_blocks = (rows + tr_exit - 1) / tr_exit;
     p.rowpart_bytes = round256((uint64_t)rows * 2u * sizeof(float));
 
     const uint64_t fused_ws = (uint64_t)p.teams * 3u * (uint64_t)d.h * sizeof(float);
     const uint64_t split_ws = p.rowpart_bytes + (uint64_t)p.row_blocks * 3u * (uint64_t)d.h * sizeof(float);
-    p.workspace = round256(fused_ws > split_ws ? fused_ws : split_ws);
+    const uint64_t exit_ws = (uint64_t)p.exit_row_blocks * (uint64_t)d.h * sizeof(float);
+    uint64_t ws = fused_ws > split_ws ? fused_ws : split_ws;
+    if (exit_ws > ws) ws = exit_ws;
+    p.workspace = round256(ws);
 
     p.path = fused_ok ? kBwdFused : kBwdSplit;
     const char* force = getenv("SPR_BWD_PATH");
@@ -428,7 +449,7 @@ spr_status sp_region_bwd_exit(const spr_desc* d, const void* dh_out, const uint8
     const uint64_t E = (uint64_t)rows * (uint64_t)d->h;
     const uint64_t es = (d->io == SPR_BF16) ? 2u : 4u;
     // slot 0 of [row_blocks][1][h] fp32 column partials
-    const size_t need = dbias_out ? (size_t)plan.row_blocks * (size_t)d->h * sizeof(float) : 0;
+    const size_t need = dbias_out ? (size_t)plan.exit_row_blocks * (size_t)d->h * sizeof(float) : 0;
     if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 16)))
         return SPR_ERR_WORKSPACE;
     const Range outs[] = {range_of(dx_out, E * es), range_of(dbias_out, (uint64_t)d->h * 4u),
@@ -443,9 +464,9 @@ spr_status sp_region_bwd_exit(const spr_desc* d, const void* dh_out, const uint8
     a.hidden = d->h;
     set_dropout(*d, rows, &a);
     a.nvec = plan.rows.nvec;
-    a.teams = (int)plan.row_blocks;
+    a.teams = (int)plan.exit_row_blocks;
     a.col_tiles = plan.col_tiles;
-    a.tile_rows = plan.tile_rows;
+    a.tile_rows = plan.exit_tile_rows;
     a.slots = 1;
     return launch_bwd_exit(*d, plan, a, stream) == hipSuccess ? SPR_OK : SPR_ERR_HIP;
 }

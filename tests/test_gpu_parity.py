@@ -99,6 +99,26 @@ def test_small_shapes(name):
              paths=(None, "fused", "split"), fwd_paths=(None, "rows", "stream"))
 
 
+# Rows per tile of the split path's second pass and of the exit (16 and 32
+# by default): other tilings must give results within the same tolerances,
+# on shapes whose last tile is ragged.
+@pytest.mark.parametrize("tile_rows", ["16", "48", "64"])
+def test_split_tile_rows(tile_rows):
+    with P._env("SPR_BWD_TILE_ROWS", tile_rows):
+        run_case(f"split tiles of {tile_rows} rows", base(s_local=1003, b=1, h=6144, offset=3),
+                 seed=11, with_dh_out=True, paths=("split",))
+        run_case(f"split tiles of {tile_rows} rows, fp32 RMS",
+                 base(s_local=37, b=3, h=3076, io=F32, norm=RMS, p=0.3), seed=12,
+                 paths=("split",))
+
+
+@pytest.mark.parametrize("tile_rows", ["32", "64"])
+def test_norm_free_exit_tile_rows(tile_rows):
+    with P._env("SPR_BWD_TILE_ROWS", tile_rows):
+        test_norm_free_exit("bf16_h8192_1100_rows")
+        test_norm_free_exit("fp32_h260_ragged_p0.3")
+
+
 # The mask-free region: the forward stores no mask and the backward
 # regenerates the decisions from the same generator words.
 MASK_FREE = {
