@@ -281,16 +281,7 @@ __global__ void __launch_bounds__(256) sp_region_bwd_finalize_kernel(BwdArgs a) 
 // w, w + 4, ... and prefetch the next group of U rows while computing the
 // current one; dx/dresidual are written and the dgamma/dbeta/dbias column
 // partials of the tile's rows are added across the waves in wave order.
-#ifndef SPR_SPLIT_U
-#define SPR_SPLIT_U 4
-#endif
-#ifndef SPR_SPLIT_PREFETCH
-#define SPR_SPLIT_PREFETCH 1
-#endif
-#ifndef SPR_EXIT_U
-#define SPR_EXIT_U 4
-#endif
-constexpr int kSplitWaves = 4, kSplitUnroll = SPR_SPLIT_U, kExitUnroll = SPR_EXIT_U;
+constexpr int kSplitWaves = 4, kSplitUnroll = 4;
 
 template <typename IO, int NORM, int VPT, bool WAVE_ROWS, int LB, bool EXACT>
 __global__ void __launch_bounds__(LB) sp_region_bwd_rowsum_kernel(BwdArgs a) {
@@ -472,21 +463,13 @@ __global__ void __launch_bounds__(256) sp_region_bwd_main_kernel(BwdArgs a) {
 
     // Trip counts differ between waves (ragged tiles) but nothing in the loop
     // synchronises the workgroup.
-    if constexpr (SPR_SPLIT_PREFETCH) {
-        TileIn<U, MW> cur, nxt;
-        int64_t base = r0 + wave;
-        if (base < r1) load_group(base, cur);
-        for (; base < r1; base += step) {
-            if (base + step < r1) load_group(base + step, nxt);
-            process_group(base, cur);
-            cur = nxt;
-        }
-    } else {
-        for (int64_t base = r0 + wave; base < r1; base += step) {
-            TileIn<U, MW> cur;
-            load_group(base, cur);
-            process_group(base, cur);
-        }
+    TileIn<U, MW> cur, nxt;
+    int64_t base = r0 + wave;
+    if (base < r1) load_group(base, cur);
+    for (; base < r1; base += step) {
+        if (base + step < r1) load_group(base + step, nxt);
+        process_group(base, cur);
+        cur = nxt;
     }
     split_store_colpart<E>(a, sh, acc_g, 0, vec, ok);
     split_store_colpart<E>(a, sh, acc_b, 1, vec, ok);
@@ -510,7 +493,7 @@ struct ExitIn {
 template <typename IO, int DROP>
 __global__ void __launch_bounds__(256) sp_region_bwd_exit_kernel(BwdArgs a) {
     using V = Vec<IO>;
-    constexpr int E = V::N, U = kExitUnroll, MW = E / 4;
+    constexpr int E = V::N, U = kSplitUnroll, MW = E / 4;
     __shared__ float sh[kSplitWaves][64][E];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
