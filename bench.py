@@ -313,15 +313,31 @@ def bench_attention(args, w):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
-    # the merge alone, on the same workspace: the step kernel is the rest
-    m0, m1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    m0.record(stream)
-    for _ in range(args.steps):
-        spr.sp_ring_attn_merge(d, o, lse, ws, stream)
-    m1.record(stream)
-    torch.cuda.synchronize()
-    merge_us = m0.elapsed_time(m1) / args.steps * 1e3
-    step_us = ms * 1e3 - merge_us
+    # Per-kernel times: the fused forward launched one index at a time (0: the
+    # ring steps, 1: the merge of their partials), a HIP graph of 10 launches
+    # of one index replayed between events on the launch stream.
+    chunk = 10
+    n_chunks = max(1, args.steps // chunk)
+    cap_stream = torch.cuda.Stream()
+    kernel_us = []
+    for idx in range(spr.sp_ring_attn_fwd_num_launches(d)):
+        g = torch.cuda.CUDAGraph()
+        cap_stream.wait_stream(stream)
+        with torch.cuda.graph(g, stream=cap_stream):
+            for _ in range(chunk):
+                spr.sp_ring_attn_fwd_launch(d, idx, q, k, v, o, lse, ws, None)
+        stream.wait_stream(cap_stream)
+        g.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for _ in range(n_chunks):
+            g.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        kernel_us.append(g0.elapsed_time(g1) / (n_chunks * chunk) * 1e3)
+        del g
+    step_us, merge_us = kernel_us
     tflops = w.flops / (step_us * 1e-6) / 1e12
     out = {
         "metric": ATTN_METRIC, "value": round(w.s_local / (ms / 1e3), 1), "unit": "tokens/s",
@@ -331,8 +347,9 @@ def bench_attention(args, w):
         "config": {"workload": w.name, "s": w.s, "t": w.t, "rank": 0, "queries": w.s_local,
                    "b": w.b, "heads": w.heads, "head_dim": w.d, "causal": False},
         "tflops": round(w.flops / (ms * 1e-3) / 1e12, 1),
-        "kernels_us": {"ring_attn_step_kernel (t steps)": round(step_us, 2),
+        "kernels_us": {"ring_attn_step_kernel": round(step_us, 2),
                        "ring_attn_merge_kernel": round(merge_us, 2)},
+        "kernel_timing": "HIP events around replays of a HIP graph of 10 launches of one kernel",
         "roofline": {"bound": "mfma", "kernel": "ring_attn_step_kernel", "achieved": round(tflops, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,

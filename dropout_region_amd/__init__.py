@@ -119,6 +119,10 @@ def lib():
         L.sp_ring_attn_step.restype = ctypes.c_int
         L.sp_ring_attn_merge.argtypes = [A, P, P, P, ctypes.c_size_t, P]
         L.sp_ring_attn_merge.restype = ctypes.c_int
+        L.sp_ring_attn_fwd_num_launches.argtypes = [A]
+        L.sp_ring_attn_fwd_num_launches.restype = ctypes.c_int
+        L.sp_ring_attn_fwd_launch.argtypes = [A, ctypes.c_int, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.sp_ring_attn_fwd_launch.restype = ctypes.c_int
         L.sp_region_status_string.argtypes = [ctypes.c_int]
         L.sp_region_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -291,6 +295,23 @@ def sp_ring_attn_fwd(d, q, k, v, o_out, lse_out, workspace, stream=None):
                                 *_ws(workspace), _stream(stream))
     if st != SPR_OK:
         raise SprError("sp_ring_attn_fwd", st)
+
+
+def sp_ring_attn_fwd_num_launches(d):
+    return int(lib().sp_ring_attn_fwd_num_launches(ctypes.byref(d.c())))
+
+
+def sp_ring_attn_fwd_launch(d, index, q, k, v, o_out, lse_out, workspace, stream=None):
+    import torch
+    n, dev = d.rows * d.d, q.device if q is not None else None
+    bf = torch.bfloat16
+    st = lib().sp_ring_attn_fwd_launch(ctypes.byref(d.c()), int(index), _arg(q, "q", n, bf, dev),
+                                       _arg(k, "k", d.t * n, bf, dev), _arg(v, "v", d.t * n, bf, dev),
+                                       _arg(o_out, "o_out", n, bf, dev),
+                                       _arg(lse_out, "lse_out", d.rows, torch.float32, dev, True),
+                                       *_ws(workspace), _stream(stream))
+    if st != SPR_OK:
+        raise SprError("sp_ring_attn_fwd_launch", st)
 
 
 def sp_ring_attn_step(d, step, q, k_blk, v_blk, workspace, stream=None):

@@ -407,12 +407,15 @@ static hipError_t launch_step(const AttnArgs& a, int steps, hipStream_t s) {
 }
 
 template <int D>
-static hipError_t launch_attn(const AttnArgs& a, int steps, bool merge, hipStream_t s) {
+static hipError_t launch_attn(const AttnArgs& a, int steps, bool step, bool merge, hipStream_t s) {
     // Eight waves: each staged tile serves 256 queries (the staging registers
     // and the L2 -> LDS traffic per query halve against four waves).
-    hipError_t e = a.spg > 1 ? launch_step<D, kWaves, true>(a, steps, s)
-                             : launch_step<D, kWaves, false>(a, steps, s);
-    if (e != hipSuccess || !merge) return e;
+    if (step) {
+        const hipError_t e = a.spg > 1 ? launch_step<D, kWaves, true>(a, steps, s)
+                                       : launch_step<D, kWaves, false>(a, steps, s);
+        if (e != hipSuccess) return e;
+    }
+    if (!merge) return hipSuccess;
     const int64_t nrows = a.s_local * a.b * a.heads;
     const int64_t rpb = 256 / (D / 4);
     hipLaunchKernelGGL(ring_attn_merge_kernel<D>, dim3((unsigned)((nrows + rpb - 1) / rpb)),
@@ -420,10 +423,13 @@ static hipError_t launch_attn(const AttnArgs& a, int steps, bool merge, hipStrea
     return hipGetLastError();
 }
 
-hipError_t launch_ring_attn(int d, const AttnArgs& a, int steps, bool merge, hipStream_t s) {
+// steps: groups of ring steps in the step launch; step / merge: which of the
+// two launches to make.
+hipError_t launch_ring_attn(int d, const AttnArgs& a, int steps, bool step, bool merge,
+                            hipStream_t s) {
     switch (d) {
-        case 64: return launch_attn<64>(a, steps, merge, s);
-        case 128: return launch_attn<128>(a, steps, merge, s);
+        case 64: return launch_attn<64>(a, steps, step, merge, s);
+        case 128: return launch_attn<128>(a, steps, step, merge, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -462,9 +468,10 @@ uint64_t workspace_need(const spr_attn_desc* d) {
 // Ring steps per workgroup in the fused call: the largest divisor k of t
 // that still leaves at least 256 workgroups (one per CU), so each workgroup
 // walks a longer run of key tiles and the merge folds t / k partials instead
-// of t (measured on MI355X, 4096 queries x 32768 keys: 4 steps per workgroup
-// 529 us, 2: 544, 1: 557).  SPR_ATTN_STEPS_PER_WG=k asks for k (a divisor of
-// t; tests check several).
+// of t (measured on MI355X, 4096 queries x 32768 keys, t = 8, the whole
+// fused call: 4 steps per workgroup 549 us, 2: 565, 1: 600, 8 -- half the
+// CUs idle -- 924).  SPR_ATTN_STEPS_PER_WG=k asks for k (a divisor of t;
+// tests check several).
 int steps_per_workgroup(const spr_attn_desc* d) {
     const char* env = getenv("SPR_ATTN_STEPS_PER_WG");
     if (env) {
@@ -520,7 +527,7 @@ spr_status sp_ring_attn_step(const spr_attn_desc* d, int32_t step, const void* q
     a.v = static_cast<const __bf16*>(v_blk);
     a.step0 = step;
     a.fused = 0;
-    return launch_ring_attn(d->d, a, 1, false, stream) == hipSuccess ? SPR_OK : SPR_ERR_HIP;
+    return launch_ring_attn(d->d, a, 1, true, false, stream) == hipSuccess ? SPR_OK : SPR_ERR_HIP;
 }
 
 spr_status sp_ring_attn_merge(const spr_attn_desc* d, void* o_out, float* lse_out,
@@ -536,20 +543,13 @@ spr_status sp_ring_attn_merge(const spr_attn_desc* d, void* o_out, float* lse_ou
     AttnArgs a = make_args(d, workspace);
     a.o_out = static_cast<__bf16*>(o_out);
     a.lse_out = lse_out;
-    const int64_t nrows = (int64_t)rows_of(d);
-    const int64_t rpb = 256 / (d->d / 4);
-    if (d->d == 64)
-        hipLaunchKernelGGL(ring_attn_merge_kernel<64>, dim3((unsigned)((nrows + rpb - 1) / rpb)),
-                           dim3(256), 0, stream, a);
-    else
-        hipLaunchKernelGGL(ring_attn_merge_kernel<128>, dim3((unsigned)((nrows + rpb - 1) / rpb)),
-                           dim3(256), 0, stream, a);
-    return hipGetLastError() == hipSuccess ? SPR_OK : SPR_ERR_HIP;
+    return launch_ring_attn(d->d, a, 0, false, true, stream) == hipSuccess ? SPR_OK : SPR_ERR_HIP;
 }
 
-spr_status sp_ring_attn_fwd(const spr_attn_desc* d, const void* q, const void* k,
-                            const void* v, void* o_out, float* lse_out, void* workspace,
-                            size_t workspace_bytes, hipStream_t stream) {
+// Every check of the fused forward, then its launch arguments.
+static spr_status prepare_fwd(const spr_attn_desc* d, const void* q, const void* k, const void* v,
+                              void* o_out, float* lse_out, void* workspace,
+                              size_t workspace_bytes, AttnArgs* out) {
     if (!attn_desc_ok(d)) return SPR_ERR_INVALID_ARG;
     if (!q || !k || !v || !o_out) return SPR_ERR_INVALID_ARG;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o_out, 16) ||
@@ -572,7 +572,32 @@ spr_status sp_ring_attn_fwd(const spr_attn_desc* d, const void* q, const void* k
     a.fused = 1;
     a.spg = steps_per_workgroup(d);
     a.nparts = d->t / a.spg;
-    return launch_ring_attn(d->d, a, a.nparts, true, stream) == hipSuccess ? SPR_OK : SPR_ERR_HIP;
+    *out = a;
+    return SPR_OK;
+}
+
+spr_status sp_ring_attn_fwd(const spr_attn_desc* d, const void* q, const void* k,
+                            const void* v, void* o_out, float* lse_out, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+    AttnArgs a;
+    const spr_status st = prepare_fwd(d, q, k, v, o_out, lse_out, workspace, workspace_bytes, &a);
+    if (st != SPR_OK) return st;
+    return launch_ring_attn(d->d, a, a.nparts, true, true, stream) == hipSuccess ? SPR_OK
+                                                                                 : SPR_ERR_HIP;
+}
+
+int sp_ring_attn_fwd_num_launches(const spr_attn_desc* d) { return attn_desc_ok(d) ? 2 : 0; }
+
+spr_status sp_ring_attn_fwd_launch(const spr_attn_desc* d, int index, const void* q, const void* k,
+                                   const void* v, void* o_out, float* lse_out, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream) {
+    AttnArgs a;
+    const spr_status st = prepare_fwd(d, q, k, v, o_out, lse_out, workspace, workspace_bytes, &a);
+    if (st != SPR_OK) return st;
+    if (index < 0 || index > 1) return SPR_ERR_INVALID_ARG;
+    return launch_ring_attn(d->d, a, a.nparts, index == 0, index == 1, stream) == hipSuccess
+               ? SPR_OK
+               : SPR_ERR_HIP;
 }
 
 }  // extern "C"

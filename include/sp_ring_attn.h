@@ -79,6 +79,20 @@ spr_status sp_ring_attn_step(const spr_attn_desc* desc, int32_t step, const void
 spr_status sp_ring_attn_merge(const spr_attn_desc* desc, void* o_out, float* lse_out,
                               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* sp_ring_attn_fwd is two kernel launches on `stream`: the ring steps (index
+ * 0; each workgroup may walk several consecutive steps and write one partial
+ * for them), then the merge of those partials (index 1).  These two let a
+ * caller run them one at a time -- to time each kernel with events on the
+ * stream; launching indices 0 and 1 in order on one stream is exactly
+ * sp_ring_attn_fwd.  Same arguments and checks as sp_ring_attn_fwd.
+ * sp_ring_attn_fwd_num_launches returns 0 for an invalid desc;
+ * sp_ring_attn_fwd_launch returns SPR_ERR_INVALID_ARG for an index outside
+ * 0 .. n-1 (after the other checks, before any launch). */
+int sp_ring_attn_fwd_num_launches(const spr_attn_desc* desc);
+spr_status sp_ring_attn_fwd_launch(const spr_attn_desc* desc, int index, const void* q,
+                                   const void* k, const void* v, void* o_out, float* lse_out,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

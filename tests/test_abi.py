@@ -36,7 +36,8 @@ def test_header_declares_the_boundary():
                             "sp_region_bwd_num_launches", "sp_region_bwd_launch",
                             "sp_region_activation_bytes", "sp_region_status_string",
                             "sp_ring_attn_workspace_bytes", "sp_ring_attn_fwd",
-                            "sp_ring_attn_step", "sp_ring_attn_merge"])
+                            "sp_ring_attn_step", "sp_ring_attn_merge",
+                            "sp_ring_attn_fwd_num_launches", "sp_ring_attn_fwd_launch"])
 
 
 def test_library_exports_every_declared_function(L):
@@ -224,6 +225,29 @@ def test_ring_attn_rejects_bad_calls(L):
                                                            for i in range(3)],
                                    ctypes.c_void_p(A + 0x8000000), ctypes.c_size_t(need),
                                    None) == spr.SPR_ERR_INVALID_ARG
+
+
+def test_ring_attn_launch_count_and_index(L):
+    """The fused forward is two launches; an index outside them, or a bad
+    desc, is rejected before anything is launched."""
+    def desc(**kw):
+        base = dict(s_local=128, b=1, heads=2, d=128, t=4, rank=1, scale=0.0)
+        base.update(kw)
+        return spr.AttnDesc(**base).c()
+    d = desc()
+    assert L.sp_ring_attn_fwd_num_launches(ctypes.byref(d)) == 2
+    assert L.sp_ring_attn_fwd_num_launches(ctypes.byref(desc(d=96))) == 0
+    need = L.sp_ring_attn_workspace_bytes(ctypes.byref(d))
+    ptrs = [ctypes.c_void_p(A + i * 0x1000000) for i in range(5)]
+    for index in (-1, 2):
+        assert L.sp_ring_attn_fwd_launch(ctypes.byref(d), index, *ptrs,
+                                         ctypes.c_void_p(A + 0x8000000), ctypes.c_size_t(need),
+                                         None) == spr.SPR_ERR_INVALID_ARG, index
+    assert L.sp_ring_attn_fwd_launch(ctypes.byref(desc(rank=4)), 0, *ptrs,
+                                     ctypes.c_void_p(A + 0x8000000), ctypes.c_size_t(need),
+                                     None) == spr.SPR_ERR_INVALID_ARG
+    assert L.sp_ring_attn_fwd_launch(ctypes.byref(d), 0, *ptrs, ctypes.c_void_p(A + 0x8000000),
+                                     ctypes.c_size_t(need - 1), None) == spr.SPR_ERR_WORKSPACE
 
 
 def test_activation_bytes_count_the_buffers_a_forward_keeps(L):

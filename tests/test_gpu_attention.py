@@ -99,6 +99,29 @@ def test_steps_in_any_order_then_merge_equal_the_fused_call():
     P.exact("o (steps + merge vs fused)", P.to_host(o), P.to_host(o_f))
 
 
+@pytest.mark.parametrize("spg", [None, "2", "4"])
+def test_launch_by_launch_equals_the_fused_call(spg):
+    """Launching the fused forward's two kernels one at a time on the stream
+    (the ring steps, then the merge) gives the bits of sp_ring_attn_fwd."""
+    import torch
+    kw = dict(s_local=160, b=2, heads=2, d=128, t=4, rank=3)
+    d = spr.AttnDesc(**kw)
+    _say(f"[case] ring attention launch by launch: {kw} steps per workgroup {spg or 'auto'}")
+    x = make_attn_inputs(d.s_local, d.b, d.heads, d.d, d.t, seed=12)
+    q, k, v = _dev(x["q"]), _dev(x["k"]), _dev(x["v"])
+    assert spr.sp_ring_attn_fwd_num_launches(d) == 2
+    with P._env("SPR_ATTN_STEPS_PER_WG", spg):
+        o_f, lse_f = spr.ring_attn(d, q, k, v)
+        o = torch.empty_like(o_f)
+        lse = torch.empty_like(lse_f)
+        ws = torch.zeros(spr.sp_ring_attn_workspace_bytes(d), dtype=torch.uint8, device=q.device)
+        for i in range(2):
+            spr.sp_ring_attn_fwd_launch(d, i, q, k, v, o, lse, ws)
+    torch.cuda.synchronize()
+    P.exact("o (launch by launch vs fused)", P.to_host(o), P.to_host(o_f))
+    P.exact("lse (launch by launch vs fused)", P.to_host(lse), P.to_host(lse_f))
+
+
 def test_rank_changes_only_the_order():
     """Every rank of the ring sees the same keys in a different order: the
     results agree within the tolerance (and each matches the oracle)."""
