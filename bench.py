@@ -395,7 +395,7 @@ def main():
     if args.counters_summary:
         return counters_summary(args.counters_summary, wname, args.command)
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: the benchmark runs on one GPU; --gpus {args.gpus} is not supported "
               "(the region is per-rank; there are no collectives to run)", file=sys.stderr)
         sys.exit(2)
 
