@@ -77,6 +77,28 @@ def make_attn_inputs(s_local, b, heads, d, t, seed=0):
     return {"q": to_bf16_bits(q), "k": to_bf16_bits(k), "v": to_bf16_bits(v)}
 
 
+def make_attn_inputs_ramp(s_local, b, heads, d, t, seed=0, span=200.0, rising=True):
+    """Ring attention whose scores climb (rising) or fall steadily along the
+    global key index j of the S = t * s_local key tokens: every element of q
+    is 1 + 0.05 N(0,1); key j is g_j (1 + 0.05 N(0,1)) per element with
+    g_j = c j / (S - 1) (rising) or c (S - 1 - j) / (S - 1), c chosen so that
+    the scaled scores q.k / sqrt(d) span about `span` in base-2 units; v is
+    standard normal.  Drawn from default_rng(seed + 3) in the order q, k, v,
+    as bf16 bits.  A streaming softmax must move its reference many times on
+    such keys (or, falling, almost never)."""
+    rng = np.random.default_rng(seed + 3)
+    S = t * s_local
+    n = s_local * b * heads * d
+    c = span / (np.sqrt(d) * np.log2(np.e))
+    q = 1.0 + 0.05 * rng.standard_normal(n)
+    j = np.arange(S, dtype=np.float64)
+    g = c * (j if rising else (S - 1 - j)) / max(S - 1, 1)
+    k = (1.0 + 0.05 * rng.standard_normal((S, b * heads * d))) * g[:, None]
+    v = rng.standard_normal(t * n)
+    f = lambda a: to_bf16_bits(np.asarray(a, dtype=np.float32).reshape(-1))
+    return {"q": f(q), "k": f(k), "v": f(v)}
+
+
 @dataclass
 class Workload:
     """One shard shape and region setting (sizes as the pages' layers)."""

@@ -15,7 +15,7 @@ import pytest
 
 import dropout_region_amd as spr
 import oracle
-from sp_inputs import make_attn_inputs
+from sp_inputs import make_attn_inputs, make_attn_inputs_ramp
 from tests import parity as P
 
 pytestmark = pytest.mark.gpu
@@ -74,6 +74,32 @@ def test_ring_attention_matches_oracle(name):
     mid = [str(k) for k in range(2, d.t) if d.t % k == 0][:1]   # a proper divisor, if any
     for spg in sorted({None, "1", str(d.t), *mid}, key=str):
         _say(f"[case] ring attention {name}: {kw}, steps per workgroup {spg}")
+        with P._env("SPR_ATTN_STEPS_PER_WG", spg):
+            o, lse = spr.ring_attn(d, _dev(x["q"]), _dev(x["k"]), _dev(x["v"]))
+        check_attention(f"{name} spg {spg}", P.to_host(o), P.to_host(lse), want_o, want_lse,
+                        x["v"])
+
+
+# Scores that climb along the key sequence by ~200 (base 2) make the streaming
+# softmax move its reference (and rescale O) many times, within a tile run,
+# across ring-step blocks and in the ring's non-monotone block order; falling
+# scores leave the first tile's reference in place.
+RAMP = {
+    "d64_rising_t4_rank1": (dict(s_local=150, b=1, heads=2, d=64, t=4, rank=1), True),
+    "d128_falling_t3_rank2": (dict(s_local=200, b=2, heads=1, d=128, t=3, rank=2), False),
+    "d128_rising_t8_rank5": (dict(s_local=70, b=1, heads=1, d=128, t=8, rank=5), True),
+}
+
+
+@pytest.mark.parametrize("name", sorted(RAMP))
+def test_softmax_reference_moves(name):
+    kw, rising = RAMP[name]
+    d, od = spr.AttnDesc(**kw), oracle.AttnDesc(**kw)
+    x = make_attn_inputs_ramp(d.s_local, d.b, d.heads, d.d, d.t,
+                              seed=zlib.crc32(name.encode()) % 1000, rising=rising)
+    want_o, want_lse = oracle.attention(od, x["q"], x["k"], x["v"])
+    for spg in sorted({None, "1", str(d.t)}, key=str):
+        _say(f"[case] ring attention, moving reference {name}: {kw}, steps per workgroup {spg}")
         with P._env("SPR_ATTN_STEPS_PER_WG", spg):
             o, lse = spr.ring_attn(d, _dev(x["q"]), _dev(x["k"]), _dev(x["v"]))
         check_attention(f"{name} spg {spg}", P.to_host(o), P.to_host(lse), want_o, want_lse,
