@@ -273,9 +273,16 @@ __device__ __forceinline__ MeanM2 merge(MeanM2 a, MeanM2 b) {
     return {n, a.mean + d * wb, a.m2 + b.m2 + d * d * a.n * wb};
 }
 
-// Team-wide merge of per-thread (count, mean, M2): wave butterflies, then the
-// waves' results in wave order through `slot` (3 x 16 floats of LDS).
-__device__ __forceinline__ MeanM2 block_mean_m2(MeanM2 v, float* slot, int nwaves) {
+// Team-wide merge of per-thread (count, mean, M2), the means taken relative
+// to a pivot `piv` that is the same across each wave (a value of the row):
+// wave butterflies, then the waves' results in wave order through `slot`
+// (4 x 16 floats of LDS), each wave's mean first moved into wave 0's frame
+// ((piv_w - piv_0) + mean_w, both differences of nearby values).  Returns
+// the merge relative to wave 0's pivot, which `piv0` receives.  With the
+// pivots the merged means stay of the size of the row's spread, not of its
+// mean, so a row whose mean is many times its spread keeps its variance.
+__device__ __forceinline__ MeanM2 block_mean_m2(MeanM2 v, float piv, float* slot, int nwaves,
+                                                float& piv0) {
     const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int off = 1; off <= 32; off <<= 1) {
@@ -284,12 +291,17 @@ __device__ __forceinline__ MeanM2 block_mean_m2(MeanM2 v, float* slot, int nwave
         const bool upper = (lane & off) != 0;
         v = merge(upper ? o : v, upper ? v : o);
     }
+    piv0 = piv;
     if (nwaves == 1) return v;
     const int wave = threadIdx.x >> 6;
-    if (lane == 0) { slot[wave] = v.n; slot[16 + wave] = v.mean; slot[32 + wave] = v.m2; }
+    if (lane == 0) {
+        slot[wave] = v.n; slot[16 + wave] = v.mean; slot[32 + wave] = v.m2; slot[48 + wave] = piv;
+    }
     __syncthreads();
+    piv0 = slot[48];
     MeanM2 acc{slot[0], slot[16], slot[32]};
-    for (int w = 1; w < nwaves; ++w) acc = merge(acc, MeanM2{slot[w], slot[16 + w], slot[32 + w]});
+    for (int w = 1; w < nwaves; ++w)
+        acc = merge(acc, MeanM2{slot[w], (slot[48 + w] - piv0) + slot[16 + w], slot[32 + w]});
     return acc;
 }
 

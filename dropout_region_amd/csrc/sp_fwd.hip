@@ -29,11 +29,11 @@ namespace spr {
 // masked afterwards).
 
 // Dropout decisions, h = residual + dropout(x + bias) and its stores (h, and
-// the mask when p > 0); returns the thread's sum of its h values.  Element
+// the mask when p > 0).  Element
 // (row, c) is element e = (row_base + row)*h + c of the full tensor; its
 // word is word e%4 of Philox block e/4.
 template <typename IO, bool DROP, int VPT>
-__device__ __forceinline__ float fwd_dropout_residual(const FwdArgs& a, int64_t row,
+__device__ __forceinline__ void fwd_dropout_residual(const FwdArgs& a, int64_t row,
                                                       const int (&vc)[VPT], const bool (&ok)[VPT],
                                                       const uint4 (&xq)[VPT], const uint4 (&rq)[VPT],
                                                       const float (&bb)[VPT][Vec<IO>::N],
@@ -42,20 +42,16 @@ __device__ __forceinline__ float fwd_dropout_residual(const FwdArgs& a, int64_t 
     constexpr int MW = E / 4;                 // mask words per vector
     const int64_t rbase = row * a.hidden;
     if (!a.x) {                               // norm-only entry: h is the residual, bit for bit
-        float sum = 0.0f;
 #pragma unroll
         for (int k = 0; k < VPT; ++k) {
             Vec<IO> r;
             r.set(rq[k]);
 #pragma unroll
             for (int j = 0; j < E; ++j) hv[k][j] = r.v[j];
-            if (ok[k]) {
-#pragma unroll
-                for (int j = 0; j < E; ++j) sum += hv[k][j];
-                if (a.h_out) store_stream(static_cast<IO*>(a.h_out) + rbase + (int64_t)vc[k] * E, rq[k]);
-            }
+            if (ok[k] && a.h_out)
+                store_stream(static_cast<IO*>(a.h_out) + rbase + (int64_t)vc[k] * E, rq[k]);
         }
-        return sum;
+        return;
     }
     bool keep[VPT][E];
 #pragma unroll
@@ -71,14 +67,11 @@ __device__ __forceinline__ float fwd_dropout_residual(const FwdArgs& a, int64_t 
             for (int j = 0; j < E; ++j) keep[k][j] = true;   // p == 0: scale is exactly 1
         }
     }
-    float sum = 0.0f;
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
         uint4 hw;
         HVec<IO>::compute(xq[k], rq[k], bb[k], keep[k], DROP ? a.scale : 1.0f, hw, hv[k]);
         if (ok[k]) {
-#pragma unroll
-            for (int j = 0; j < E; ++j) sum += hv[k][j];
             const int64_t off = rbase + (int64_t)vc[k] * E;
             store_stream(static_cast<IO*>(a.h_out) + off, hw);
             if (DROP && a.mask_out) {         // no mask stored: the backward regenerates it
@@ -89,36 +82,51 @@ __device__ __forceinline__ float fwd_dropout_residual(const FwdArgs& a, int64_t 
             }
         }
     }
-    return sum;
 }
 
 // The row's statistics over the team (one block reduction through `red`):
-// LayerNorm merges each thread's (count, mean, M2) (Chan et al.); RMSNorm
-// sums squares.  Returns mean (0 for RMSNorm) and rstd.
+// LayerNorm merges each thread's (count, mean, M2) (Chan et al.), the means
+// relative to a pivot (a value of the row, lane 0's first, per wave) so that
+// a row whose mean dwarfs its spread keeps its variance; RMSNorm sums
+// squares.  Returns mean (0 for RMSNorm), rstd, and for LayerNorm the pivot
+// `piv` and the mean relative to it, `mrel` (mean = piv + mrel, rounded).
 template <int NORM, int VPT, int E>
 __device__ __forceinline__ void fwd_stats(const FwdArgs& a, const bool (&ok)[VPT],
-                                          const float (&hv)[VPT][E], float sum, float* red,
-                                          int nwaves, float& mean, float& rstd) {
+                                          const float (&hv)[VPT][E], float* red, int nwaves,
+                                          float& mean, float& rstd, float& piv, float& mrel) {
     float var;
     mean = 0.0f;
+    piv = 0.0f;
+    mrel = 0.0f;
     if (NORM == SPR_LAYERNORM) {
-        float n = 0.0f;
+        // lane 0's first slot holds a value of the row (an idle slot re-reads
+        // the row's last vector), uniform over the wave
+        const float wpiv = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(hv[0][0])));
+        float n = 0.0f, s = 0.0f;
 #pragma unroll
-        for (int k = 0; k < VPT; ++k) n += ok[k] ? (float)E : 0.0f;
-        const float m_loc = n > 0.0f ? sum / n : 0.0f;
+        for (int k = 0; k < VPT; ++k) {
+            if (ok[k]) {
+                n += (float)E;
+#pragma unroll
+                for (int j = 0; j < E; ++j) s += hv[k][j] - wpiv;
+            }
+        }
+        const float m_loc = n > 0.0f ? s / n : 0.0f;       // relative to wpiv
+        const float m_abs = wpiv + m_loc;
         float m2 = 0.0f;
 #pragma unroll
         for (int k = 0; k < VPT; ++k) {
             if (ok[k]) {
 #pragma unroll
                 for (int j = 0; j < E; ++j) {
-                    const float d = hv[k][j] - m_loc;
+                    const float d = hv[k][j] - m_abs;
                     m2 = fmaf(d, d, m2);
                 }
             }
         }
-        const MeanM2 st = block_mean_m2(MeanM2{n, m_loc, m2}, red, nwaves);
-        mean = st.mean;
+        const MeanM2 st = block_mean_m2(MeanM2{n, m_loc, m2}, wpiv, red, nwaves, piv);
+        mrel = st.mean;
+        mean = piv + mrel;
         var = st.m2 * a.inv_h;
     } else {
         float sq = 0.0f;
@@ -141,9 +149,8 @@ __device__ __forceinline__ void fwd_store_y(const FwdArgs& a, int64_t row, int t
                                             const float (&hv)[VPT][Vec<IO>::N],
                                             const float (&g)[VPT][Vec<IO>::N],
                                             const float (&bt)[VPT][Vec<IO>::N], float mean,
-                                            float rstd) {
+                                            float rstd, float piv, float mrel) {
     constexpr int E = Vec<IO>::N;
-    const float shift = -mean * rstd;                   // xhat = h * rstd + shift
     const int64_t rbase = row * a.hidden;
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
@@ -151,7 +158,19 @@ __device__ __forceinline__ void fwd_store_y(const FwdArgs& a, int64_t row, int t
             Vec<IO> yv;
 #pragma unroll
             for (int j = 0; j < E; ++j) {
-                const float xh = fmaf(hv[k][j], rstd, shift);
+                // xhat = (h - mean) * rstd: the difference is exact for h
+                // near the mean, so a row whose mean is many times its spread
+                // (a constant row: rstd = 1/sqrt(eps)) keeps xhat accurate,
+                // where h * rstd - mean * rstd would carry the rounding of
+                // mean * rstd.  fp32 output also avoids the rounding of the
+                // mean itself: (h - pivot) - mean relative to the pivot.
+                float xh;
+                if (NORM != SPR_LAYERNORM)
+                    xh = hv[k][j] * rstd;
+                else if (E == 4)                                  // fp32 I/O
+                    xh = ((hv[k][j] - piv) - mrel) * rstd;
+                else
+                    xh = (hv[k][j] - mean) * rstd;
                 yv.v[j] = (NORM == SPR_LAYERNORM) ? fmaf(xh, g[k][j], bt[k][j]) : xh * g[k][j];
             }
             yv.store(static_cast<IO*>(a.y_out) + rbase + (int64_t)vc[k] * E);
@@ -274,7 +293,7 @@ __device__ __forceinline__ void load_affine(const FwdArgs& a, const int (&vc)[VP
 template <typename IO, int NORM, bool DROP, int VPT, bool WAVE_ROWS, int LB, bool EXACT>
 __global__ void __launch_bounds__(LB) sp_region_fwd_kernel(FwdArgs a) {
     constexpr int E = Vec<IO>::N;
-    __shared__ float red[48];
+    __shared__ float red[64];
 
     int tid, tpr, nwaves;
     int64_t row;
@@ -309,14 +328,14 @@ __global__ void __launch_bounds__(LB) sp_region_fwd_kernel(FwdArgs a) {
     load_bias<VPT, E>(a, vc, bb);
 
     float hv[VPT][E];
-    const float sum = fwd_dropout_residual<IO, DROP, VPT>(a, row, vc, ok, xq, rq, bb, hv);
+    fwd_dropout_residual<IO, DROP, VPT>(a, row, vc, ok, xq, rq, bb, hv);
     if (!a.gamma) return;                // norm-free exit: h and the mask only (uniform)
 
     float g[VPT][E], bt[VPT][E];
     load_affine<NORM, VPT, E>(a, vc, g, bt);
-    float mean, rstd;
-    fwd_stats<NORM, VPT, E>(a, ok, hv, sum, red, nwaves, mean, rstd);
-    fwd_store_y<IO, NORM, VPT>(a, row, tid, vc, ok, hv, g, bt, mean, rstd);
+    float mean, rstd, piv, mrel;
+    fwd_stats<NORM, VPT, E>(a, ok, hv, red, nwaves, mean, rstd, piv, mrel);
+    fwd_store_y<IO, NORM, VPT>(a, row, tid, vc, ok, hv, g, bt, mean, rstd, piv, mrel);
 }
 
 // Stream kernel: a grid of G workgroups, about as many as fit on the chip at
@@ -331,7 +350,7 @@ __global__ void __launch_bounds__(LB) sp_region_fwd_kernel(FwdArgs a) {
 template <typename IO, int NORM, bool DROP, int VPT, int LB, bool EXACT>
 __global__ void __launch_bounds__(LB) sp_region_fwd_stream_kernel(FwdArgs a) {
     constexpr int E = Vec<IO>::N;
-    __shared__ float red[2][48];
+    __shared__ float red[2][64];
     const int tid = threadIdx.x, tpr = blockDim.x, nwaves = blockDim.x >> 6;
     const int64_t step = gridDim.x;
 
@@ -349,11 +368,11 @@ __global__ void __launch_bounds__(LB) sp_region_fwd_stream_kernel(FwdArgs a) {
 
     auto one_row = [&](int64_t r, const uint4 (&xq)[VPT], const uint4 (&rq)[VPT], float* slot) {
         float hv[VPT][E];
-        const float sum = fwd_dropout_residual<IO, DROP, VPT>(a, r, vc, ok, xq, rq, bb, hv);
+        fwd_dropout_residual<IO, DROP, VPT>(a, r, vc, ok, xq, rq, bb, hv);
         if (!a.gamma) return;            // norm-free exit (uniform)
-        float mean, rstd;
-        fwd_stats<NORM, VPT, E>(a, ok, hv, sum, slot, nwaves, mean, rstd);
-        fwd_store_y<IO, NORM, VPT>(a, r, tid, vc, ok, hv, g, bt, mean, rstd);
+        float mean, rstd, piv, mrel;
+        fwd_stats<NORM, VPT, E>(a, ok, hv, slot, nwaves, mean, rstd, piv, mrel);
+        fwd_store_y<IO, NORM, VPT>(a, r, tid, vc, ok, hv, g, bt, mean, rstd, piv, mrel);
     };
     for (;;) {
         if (row + step < a.rows) load_x_res<IO, VPT>(a, row + step, vc, xb, rb);
