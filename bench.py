@@ -535,6 +535,7 @@ def main():
         s = sets[i % nsets]
         fwd(s)
         bwd(s)
+    t_enqueued = time.perf_counter() - t0
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -578,6 +579,27 @@ def main():
         per_kernel_ms[:, k] = [evs[c].elapsed_time(evs[c + 1]) / chunk for c in range(n_chunks)]
         del g
     kernel_us = per_kernel_ms.mean(axis=0) * 1e3
+
+    # ---- whole steps (fwd then bwd) captured as a HIP graph of `chunk` steps
+    # and replayed: the GPU's step time without the host's launch path (a
+    # diagnostic; `value` is the eager step above)
+    g = torch.cuda.CUDAGraph()
+    cap_stream.wait_stream(stream)
+    with torch.cuda.graph(g, stream=cap_stream):
+        for i in range(chunk):
+            fwd(sets[i % nsets], stream=None)
+            bwd(sets[i % nsets], stream=None)
+    stream.wait_stream(cap_stream)
+    g.replay()
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record(stream)
+    for _ in range(n_chunks):
+        g.replay()
+    g1.record(stream)
+    torch.cuda.synchronize()
+    graph_step_us = g0.elapsed_time(g1) / (n_chunks * chunk) * 1e3
+    del g
 
     # ---- the reduce-scatter prologue against its unfused form (torch's sum of
     # the slabs, fp32 accumulation, into x; then sp_region_fwd), eager
@@ -688,6 +710,8 @@ def main():
         "fwd_kernel": os.environ.get("SPR_FWD_PATH", "auto"),
         "algorithmic_bytes": {"fwd": fwd_b, "bwd": bwd_rows_b + bwd_grad_b},
         "wall_s_timed_region": round(wall, 4),
+        "host_enqueue_us_per_step": round(t_enqueued / args.steps * 1e6, 2),
+        "graph_step_us": round(graph_step_us, 2),
         "roofline": {"bound": "hbm", "kernel": names[dom], "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": dom_traffic, "algorithmic_bytes_per_launch": alg[dom],
