@@ -119,6 +119,44 @@ def test_norm_free_exit_tile_rows(tile_rows):
         test_norm_free_exit("fp32_h260_ragged_p0.3")
 
 
+# Seeded random shapes: widths anywhere in the supported range (bf16: any
+# multiple of 8 up to 32768; fp32: of 4 up to 16384), 1-300 rows, either
+# norm, several p, any shard of any t -- the launch plans' corner cases
+# (ragged teams, wave rows, split backward) met at widths no list names.
+def _random_cases(n=24, seed=2024):
+    rng = np.random.default_rng(seed)
+    cases = {}
+    while len(cases) < n:
+        io = F32 if len(cases) % 3 == 2 else BF16
+        epv = 8 if io == BF16 else 4
+        hmax = 32768 if io == BF16 else 16384
+        h = int(epv * rng.integers(1, hmax // epv + 1)) if rng.random() < 0.5 else \
+            int(epv * np.exp(rng.uniform(0.0, np.log(hmax // epv))))
+        h = max(epv, min(hmax, h - h % epv))
+        rows = int(rng.integers(1, 301))
+        rows = max(1, min(rows, 3_000_000 // h))
+        b = int(rng.integers(1, 4))
+        s_local = max(1, rows // b)
+        t = int(rng.integers(1, 9))
+        norm = LN if len(cases) % 2 == 0 else RMS
+        p = float(rng.choice([0.0, 0.1, 0.5]))
+        kw = base(s_local=s_local, b=b, h=h, io=io, norm=norm, p=p, t=t,
+                  shard_index=int(rng.integers(0, t)), seed=int(rng.integers(0, 2**32)),
+                  offset=int(rng.integers(0, 2**20)), eps=1e-5 if norm == LN else 1e-6)
+        cases[f"{'bf16' if io == BF16 else 'fp32'}_{'ln' if norm == LN else 'rms'}_h{h}_"
+              f"{s_local}x{b}_p{p}_t{t}"] = kw
+    return cases
+
+
+RANDOM = _random_cases()
+
+
+@pytest.mark.parametrize("name", sorted(RANDOM))
+def test_random_shapes(name):
+    run_case(name, RANDOM[name], seed=zlib.crc32(name.encode()) % 1000,
+             with_dh_out=bool(zlib.crc32(name.encode()) & 1))
+
+
 # The mask-free region: the forward stores no mask and the backward
 # regenerates the decisions from the same generator words.
 MASK_FREE = {
