@@ -80,6 +80,35 @@ def test_ring_attention_matches_oracle(name):
                         x["v"])
 
 
+# Seeded random shapes: any s_local up to 300 (ragged key tiles, ragged
+# query tiles), batch and heads up to 3, either head size, any ring size up
+# to 8 and any rank, with the launch's own grouping of ring steps.
+def _random_attn_cases(n=12, seed=7):
+    rng = np.random.default_rng(seed)
+    cases = {}
+    while len(cases) < n:
+        t = int(rng.integers(1, 9))
+        kw = dict(s_local=int(rng.integers(1, 301)), b=int(rng.integers(1, 3)),
+                  heads=int(rng.integers(1, 4)), d=int(rng.choice([64, 128])), t=t,
+                  rank=int(rng.integers(0, t)))
+        cases["s{s_local}_b{b}_h{heads}_d{d}_t{t}_r{rank}".format(**kw)] = kw
+    return cases
+
+
+RANDOM_ATTN = _random_attn_cases()
+
+
+@pytest.mark.parametrize("name", sorted(RANDOM_ATTN))
+def test_random_attention_shapes(name):
+    kw = RANDOM_ATTN[name]
+    d, od = spr.AttnDesc(**kw), oracle.AttnDesc(**kw)
+    _say(f"[case] ring attention, random shape {name}")
+    x = make_attn_inputs(d.s_local, d.b, d.heads, d.d, d.t, seed=zlib.crc32(name.encode()) % 1000)
+    want_o, want_lse = oracle.attention(od, x["q"], x["k"], x["v"])
+    o, lse = spr.ring_attn(d, _dev(x["q"]), _dev(x["k"]), _dev(x["v"]))
+    check_attention(name, P.to_host(o), P.to_host(lse), want_o, want_lse, x["v"])
+
+
 # Scores that climb along the key sequence by ~200 (base 2) make the streaming
 # softmax move its reference (and rescale O) many times, within a tile run,
 # across ring-step blocks and in the ring's non-monotone block order; falling
