@@ -268,8 +268,9 @@ struct MeanM2 {
 };
 __device__ __forceinline__ MeanM2 merge(MeanM2 a, MeanM2 b) {
     const float n = a.n + b.n;
-    // b's weight nb / n through the hardware reciprocal (one rounding more
-    // than a division, a tenth of its instructions); both empty: (0, 0, 0)
+    // b's weight nb / n through the hardware reciprocal: two instructions
+    // instead of a correctly rounded division's ten, one rounding more;
+    // both empty: (0, 0, 0)
     const float wb = n > 0.0f ? b.n * __builtin_amdgcn_rcpf(n) : 0.0f;
     const float d = b.mean - a.mean;
     return {n, a.mean + d * wb, a.m2 + b.m2 + d * d * a.n * wb};
