@@ -51,3 +51,16 @@ def test_attention_flops():
     assert w.s_local == 4096
     # Q K^T and P V over 32768 keys: 2 * 2 * 4096 * 32768 * 128 per head, 8 heads
     assert w.flops == 4 * 4096 * 32768 * 128 * 8 == 549755813888
+
+
+def test_more_than_one_gpu_is_refused():
+    """bench.py runs on one GPU: --gpus N > 1 exits with status 2 and says so
+    (before anything touches a GPU)."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
