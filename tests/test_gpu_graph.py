@@ -69,3 +69,39 @@ def test_graph_replays_equal_eager(h, rows, fwd_path, bwd_path):
             got = P.to_host(o[k])
             assert np.array_equal(np.asarray(got).view(np.uint8), np.asarray(want[k]).view(np.uint8)), \
                 f"replay {rep}: {k} differs from the eager result"
+
+
+def test_concurrent_calls_on_two_streams_equal_serial():
+    """The library keeps no state between calls: two region calls (different
+    shapes, shards and paths' plans, separate outputs and workspaces) issued
+    on two streams at once, many times over, give the serial results bit for
+    bit."""
+    import torch
+    dev = torch.device("cuda:0")
+    cases = [(spr.Desc(s_local=96, b=2, h=6144, shard_index=3, t=4, p=0.1), 21),
+             (spr.Desc(s_local=40, b=1, h=25600, shard_index=0, t=2, p=0.2), 22)]
+    print("[case] concurrent region calls on two streams", flush=True)
+    runs = []
+    for d, seed in cases:
+        inp = make_inputs(d.rows, d.h, d.io, seed=seed, dh_out=True)
+        a = {"x": P.to_device(inp["x"], d.io), "res": P.to_device(inp["residual"], d.io),
+             "dy": P.to_device(inp["dy"], d.io), "dh_out": P.to_device(inp["dh_out"], d.io),
+             "bias": P.to_device(inp["bias"]), "gamma": P.to_device(inp["gamma"]),
+             "beta": P.to_device(inp["beta"])}
+        serial = _outputs(d, dev)
+        _run(d, a, serial)
+        torch.cuda.synchronize()
+        runs.append((d, a, {k: P.to_host(serial[k]) for k in _KEYS}, _outputs(d, dev)))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    for rep in range(20):
+        for (d, a, _, o), s in zip(runs, streams):
+            with torch.cuda.stream(s):
+                _run(d, a, o)
+    torch.cuda.synchronize()
+    for d, _, want, o in runs:
+        for k in _KEYS:
+            got = P.to_host(o[k])
+            assert np.array_equal(np.asarray(got).view(np.uint8),
+                                  np.asarray(want[k]).view(np.uint8)), f"h={d.h}: {k} differs"
