@@ -209,3 +209,50 @@ def test_full_size_workload_sampled(name):
                                             rows=(r, r + 1))
         check_attention(f"{name} query {r}", go[r * tok:(r + 1) * tok],
                         gl[r * nbh:(r + 1) * nbh], want_o, want_lse, x["v"])
+
+
+def test_graph_replays_and_concurrent_streams_equal_eager():
+    """The fused forward captured in a HIP graph and replayed (with eager
+    calls between the replays), and two calls of different shapes on two
+    streams at once, give the eager bits."""
+    import torch
+    cases = [spr.AttnDesc(s_local=300, b=1, heads=2, d=128, t=4, rank=1),
+             spr.AttnDesc(s_local=130, b=2, heads=1, d=64, t=3, rank=2)]
+    print("[case] ring attention: graph replays and two streams", flush=True)
+    runs = []
+    for i, d in enumerate(cases):
+        x = make_attn_inputs(d.s_local, d.b, d.heads, d.d, d.t, seed=30 + i)
+        q, k, v = _dev(x["q"]), _dev(x["k"]), _dev(x["v"])
+        o_e, lse_e = spr.ring_attn(d, q, k, v)
+        torch.cuda.synchronize()
+        want = (P.to_host(o_e), P.to_host(lse_e))
+        o, lse = torch.empty_like(o_e), torch.empty_like(lse_e)
+        ws = torch.zeros(spr.sp_ring_attn_workspace_bytes(d), dtype=torch.uint8, device=q.device)
+        runs.append((d, q, k, v, o, lse, ws, want))
+    d, q, k, v, o, lse, ws, want = runs[0]
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(g, stream=side):
+        spr.sp_ring_attn_fwd(d, q, k, v, o, lse, ws)
+    torch.cuda.current_stream().wait_stream(side)
+    for rep in range(3):
+        o.zero_()
+        lse.zero_()
+        spr.ring_attn(d, q, k, v)                   # eager work between the replays
+        g.replay()
+        torch.cuda.synchronize()
+        P.exact(f"o (replay {rep})", P.to_host(o), want[0])
+        P.exact(f"lse (replay {rep})", P.to_host(lse), want[1])
+    del g
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    for _ in range(10):
+        for (d, q, k, v, o, lse, ws, _), s in zip(runs, streams):
+            with torch.cuda.stream(s):
+                spr.sp_ring_attn_fwd(d, q, k, v, o, lse, ws)
+    torch.cuda.synchronize()
+    for d, q, k, v, o, lse, ws, want in runs:
+        P.exact(f"o (two streams, s_local {d.s_local})", P.to_host(o), want[0])
+        P.exact(f"lse (two streams, s_local {d.s_local})", P.to_host(lse), want[1])
