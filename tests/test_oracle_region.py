@@ -123,6 +123,28 @@ def test_forward_matches_torch_float64_norm(olib, norm, io):
         assert np.allclose(out["rstd"], 1 / np.sqrt((hh * hh).mean(axis=1) + d.eps), rtol=1e-6)
 
 
+@pytest.mark.parametrize("mean", [1.0e4, -2.0e3])
+def test_layernorm_is_shift_invariant_on_large_mean_rows(olib, mean):
+    """LayerNorm of rows whose mean is 10^3-10^4 times their spread (fp32
+    I/O, p = 0): the oracle's y equals torch's float64 layer_norm of the same
+    rounded h to one fp32 ulp, and its variance is that of the row with the
+    mean subtracted exactly (the statistics do not lose the spread to the
+    mean)."""
+    d = oracle.Desc(s_local=9, b=2, h=300, io=F32, norm=LN, p=0.0, eps=1e-5, seed=4)
+    inp = make_inputs(d.rows, d.h, F32, seed=8)
+    inp["residual"] = (np.float32(mean) + inp["residual"]).astype(np.float32)
+    out = _run_fwd(olib, d, inp)
+    h64 = out["h"].astype(np.float64).reshape(d.rows, d.h)
+    ref = torch.nn.functional.layer_norm(torch.from_numpy(h64), (d.h,),
+                                         torch.from_numpy(inp["gamma"].astype(np.float64)),
+                                         torch.from_numpy(inp["beta"].astype(np.float64)),
+                                         d.eps).numpy().astype(np.float32).ravel()
+    ulps = np.abs(out["y"].view(np.int32).astype(np.int64) - ref.view(np.int32).astype(np.int64))
+    assert ulps.max() <= 1
+    centred = h64 - h64.mean(axis=1, keepdims=True)
+    assert np.allclose(out["rstd"], 1 / np.sqrt((centred ** 2).mean(axis=1) + d.eps), rtol=1e-6)
+
+
 # ----------------------------------------------------------------- backward
 def _loss(d, ex, dy, dho):
     val = float(np.dot(dy, ex["y"]))
