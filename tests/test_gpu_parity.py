@@ -218,7 +218,11 @@ def test_reduce_scatter_prologue(name):
     parts = make_parts(d.rows, d.h, d.io, nparts, seed=seed)
     x = oracle.reduce_parts(od, parts)
     want = P.oracle_fwd(od, dict(inp, x=x))
-    got = P.gpu_fwd_rs(d, inp, parts, nparts)
+    # the row kernel on both sides (with one part, SPR_FWD_PATH=stream would
+    # otherwise send the prologue call to the stream kernel, whose reductions
+    # run in another order)
+    with P._env("SPR_FWD_PATH", "rows"):
+        got = P.gpu_fwd_rs(d, inp, parts, nparts)
     P.check_fwd(got, want, d.io)
     # bit-identical to the plain forward (same kernel) on the summed x
     plain = P.gpu_fwd(d, dict(inp, x=x), path="rows")
