@@ -142,7 +142,8 @@ def test_steps_in_any_order_then_merge_equal_the_fused_call():
     _say(f"[case] ring attention steps: {kw}")
     x = make_attn_inputs(d.s_local, d.b, d.heads, d.d, d.t, seed=9)
     q, k, v = _dev(x["q"]), _dev(x["k"]), _dev(x["v"])
-    o_f, lse_f = spr.ring_attn(d, q, k, v)
+    with P._env("SPR_ATTN_STEPS_PER_WG", "1"):        # the fused call with one step per workgroup
+        o_f, lse_f = spr.ring_attn(d, q, k, v)
     n = d.rows * d.d
     ws = torch.zeros(spr.sp_ring_attn_workspace_bytes(d), dtype=torch.uint8, device=q.device)
     for step in (3, 0, 2, 1):                      # any order: each step has its own slot
