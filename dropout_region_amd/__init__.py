@@ -135,29 +135,37 @@ def _io_dtype(d):
     return torch.bfloat16 if d.io == SPR_BF16 else torch.float32
 
 
+def _dev(t):
+    """Device index of tensor t (-1 on the host), or None for no tensor."""
+    return None if t is None else t.get_device()
+
+
 def _arg(t, name, numel, dtype, device, optional=False):
-    """Device pointer of tensor t after checking what the C side cannot:
-    device, dtype, contiguity and size."""
+    """Device pointer (an int for ctypes) of tensor t after checking what the
+    C side cannot: device (an index, as _dev gives), dtype, contiguity and
+    size.  Each check is one call into torch: this runs for every tensor of
+    every call."""
     if t is None:
         if optional:
             return None
         raise ValueError(f"{name} is required")
-    if not t.is_cuda or (device is not None and t.device != device):
-        raise ValueError(f"{name} must be on {device}")
-    if t.dtype != dtype:
+    g = t.get_device()
+    if g < 0 or (device is not None and g != device):
+        raise ValueError(f"{name} must be on GPU {device}")
+    if t.dtype is not dtype:
         raise ValueError(f"{name}: dtype {t.dtype}, want {dtype}")
     if not t.is_contiguous() or t.numel() != numel:
         raise ValueError(f"{name}: want a contiguous tensor of {numel} elements")
-    return ctypes.c_void_p(t.data_ptr())
+    return t.data_ptr()
 
 
 def _stream(stream):
     import torch
     if stream is None:
-        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        return torch.cuda.current_stream().cuda_stream
     if isinstance(stream, int):
-        return ctypes.c_void_p(stream)
-    return ctypes.c_void_p(stream.cuda_stream)
+        return stream
+    return stream.cuda_stream
 
 
 # ------------------------------------------------------------ entry points
@@ -183,7 +191,7 @@ def sp_region_fwd(d, x, bias, residual, gamma, beta, h_out, y_out, mask_out, mea
     import torch
     L = lib()
     N, H, io = d.rows, d.h, _io_dtype(d)
-    dev = residual.device if residual is not None else None
+    dev = _dev(residual)
     f32, u8 = torch.float32, torch.uint8
     args = [_arg(x, "x", N * H, io, dev, True), _arg(bias, "bias", H, f32, dev, True),
             _arg(residual, "residual", N * H, io, dev), _arg(gamma, "gamma", H, f32, dev, True),
@@ -203,7 +211,7 @@ def sp_region_fwd_rs(d, x_parts, nparts, bias, residual, gamma, beta, h_out, y_o
     ([nparts, N, h], contiguous), added in the kernel's prologue."""
     import torch
     L = lib()
-    N, H, io, dev = d.rows, d.h, _io_dtype(d), x_parts.device if x_parts is not None else None
+    N, H, io, dev = d.rows, d.h, _io_dtype(d), _dev(x_parts)
     f32, u8 = torch.float32, torch.uint8
     args = [_arg(x_parts, "x_parts", int(nparts) * N * H, io, dev), ctypes.c_int32(int(nparts)),
             _arg(bias, "bias", H, f32, dev, True),
@@ -219,7 +227,7 @@ def sp_region_fwd_rs(d, x_parts, nparts, bias, residual, gamma, beta, h_out, y_o
 def _bwd_args(d, dy, dh_out, h, mask, mean, rstd, gamma, dx_out, dres_out, dgamma_out,
               dbeta_out, dbias_out, workspace):
     import torch
-    N, H, io, dev = d.rows, d.h, _io_dtype(d), dy.device if dy is not None else None
+    N, H, io, dev = d.rows, d.h, _io_dtype(d), _dev(dy)
     f32, u8 = torch.float32, torch.uint8
     if workspace is None or not workspace.is_cuda or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous device tensor")
@@ -247,7 +255,7 @@ def sp_region_bwd(d, dy, dh_out, h, mask, mean, rstd, gamma, dx_out, dres_out, d
 def sp_region_bwd_exit(d, dh_out, mask, dx_out, dbias_out, workspace, stream=None):
     """Backward of the norm-free exit (forward with gamma = None)."""
     import torch
-    N, H, io, dev = d.rows, d.h, _io_dtype(d), dh_out.device if dh_out is not None else None
+    N, H, io, dev = d.rows, d.h, _io_dtype(d), _dev(dh_out)
     ws = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = lib().sp_region_bwd_exit(ctypes.byref(d.c()), _arg(dh_out, "dh_out", N * H, io, dev),
@@ -286,7 +294,7 @@ def _ws(workspace):
 
 def sp_ring_attn_fwd(d, q, k, v, o_out, lse_out, workspace, stream=None):
     import torch
-    n, dev = d.rows * d.d, q.device if q is not None else None
+    n, dev = d.rows * d.d, _dev(q)
     bf = torch.bfloat16
     st = lib().sp_ring_attn_fwd(ctypes.byref(d.c()), _arg(q, "q", n, bf, dev),
                                 _arg(k, "k", d.t * n, bf, dev), _arg(v, "v", d.t * n, bf, dev),
@@ -303,7 +311,7 @@ def sp_ring_attn_fwd_num_launches(d):
 
 def sp_ring_attn_fwd_launch(d, index, q, k, v, o_out, lse_out, workspace, stream=None):
     import torch
-    n, dev = d.rows * d.d, q.device if q is not None else None
+    n, dev = d.rows * d.d, _dev(q)
     bf = torch.bfloat16
     st = lib().sp_ring_attn_fwd_launch(ctypes.byref(d.c()), int(index), _arg(q, "q", n, bf, dev),
                                        _arg(k, "k", d.t * n, bf, dev), _arg(v, "v", d.t * n, bf, dev),
@@ -316,7 +324,7 @@ def sp_ring_attn_fwd_launch(d, index, q, k, v, o_out, lse_out, workspace, stream
 
 def sp_ring_attn_step(d, step, q, k_blk, v_blk, workspace, stream=None):
     import torch
-    n, dev = d.rows * d.d, q.device if q is not None else None
+    n, dev = d.rows * d.d, _dev(q)
     bf = torch.bfloat16
     st = lib().sp_ring_attn_step(ctypes.byref(d.c()), ctypes.c_int32(int(step)),
                                  _arg(q, "q", n, bf, dev), _arg(k_blk, "k_blk", n, bf, dev),
@@ -328,7 +336,7 @@ def sp_ring_attn_step(d, step, q, k_blk, v_blk, workspace, stream=None):
 
 def sp_ring_attn_merge(d, o_out, lse_out, workspace, stream=None):
     import torch
-    n, dev = d.rows * d.d, o_out.device if o_out is not None else None
+    n, dev = d.rows * d.d, _dev(o_out)
     st = lib().sp_ring_attn_merge(ctypes.byref(d.c()), _arg(o_out, "o_out", n, torch.bfloat16, dev),
                                   _arg(lse_out, "lse_out", d.rows, torch.float32, dev, True),
                                   *_ws(workspace), _stream(stream))
