@@ -291,16 +291,17 @@ def bench_attention(args, w):
 
     if not args.no_parity:                       # sampled query tokens against the oracle
         import oracle
-        from tests.test_gpu_attention import check_attention
+        from tests.attn_check import check_attention
         fwd()
         torch.cuda.synchronize()
         od = oracle.AttnDesc(s_local=w.s_local, b=w.b, heads=w.heads, d=w.d, t=w.t)
         tok, go, gl = w.b * w.heads * w.d, P.to_host(o), P.to_host(lse)
         for r in sorted({0, w.s_local // 2, w.s_local - 1}):
-            wo, wl = oracle.attention(od, x["q"][r * tok:(r + 1) * tok], x["k"], x["v"],
-                                      rows=(r, r + 1))
-            check_attention(f"query {r}", go[r * tok:(r + 1) * tok],
-                            gl[r * w.b * w.heads:(r + 1) * w.b * w.heads], wo, wl, x["v"])
+            qr = x["q"][r * tok:(r + 1) * tok]
+            wo, wl = oracle.attention(od, qr, x["k"], x["v"], rows=(r, r + 1))
+            check_attention(f"query {r}", od, qr, x["k"], x["v"], go[r * tok:(r + 1) * tok],
+                            gl[r * w.b * w.heads:(r + 1) * w.b * w.heads], wo, wl,
+                            rows=(r, r + 1))
         print("[bench] parity ok on sampled queries", file=sys.stderr, flush=True)
 
     for _ in range(args.warmup):
@@ -702,12 +703,10 @@ def main():
                    if w.p > 0 else "none (p = 0)"},
         "hbm_gbps": round(gbps, 1), "hbm_frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4),
         "copy_gbps": round(copy_gbps, 1), "frac_of_copy": round(gbps / copy_gbps, 4),
-        "bwd_path": os.environ.get("SPR_BWD_PATH", "auto"),
         "kernels_us": {n: round(float(u), 2) for n, u in zip(names, kernel_us)},
         "kernels_us_p10_p90": {n: [round(float(np.percentile(per_kernel_ms[:, k], q)) * 1e3, 2)
                                    for q in (10, 90)] for k, n in enumerate(names)},
         "kernel_timing": f"HIP events around replays of a HIP graph of {chunk} launches of one kernel",
-        "fwd_kernel": os.environ.get("SPR_FWD_PATH", "auto"),
         "algorithmic_bytes": {"fwd": fwd_b, "bwd": bwd_rows_b + bwd_grad_b},
         "wall_s_timed_region": round(wall, 4),
         "host_enqueue_us_per_step": round(t_enqueued / args.steps * 1e6, 2),

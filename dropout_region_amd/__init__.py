@@ -16,6 +16,8 @@ LIB_PATH = os.path.join(_PKG, "libsp_region.so")
 SPR_OK, SPR_ERR_INVALID_ARG, SPR_ERR_UNSUPPORTED, SPR_ERR_WORKSPACE, SPR_ERR_HIP = range(5)
 SPR_F32, SPR_BF16 = 0, 1
 SPR_LAYERNORM, SPR_RMSNORM = 0, 1
+SPR_FWD_AUTO, SPR_FWD_ROWS, SPR_FWD_STREAM = 0, 1, 2
+SPR_BWD_AUTO, SPR_BWD_FUSED, SPR_BWD_SPLIT = 0, 1, 2
 
 
 class SprError(RuntimeError):
@@ -29,12 +31,15 @@ class spr_desc(ctypes.Structure):
                 ("shard_index", ctypes.c_int32), ("t", ctypes.c_int32),
                 ("io", ctypes.c_int32), ("norm", ctypes.c_int32),
                 ("p", ctypes.c_float), ("eps", ctypes.c_float),
-                ("seed", ctypes.c_uint64), ("offset", ctypes.c_uint64)]
+                ("seed", ctypes.c_uint64), ("offset", ctypes.c_uint64),
+                ("fwd_kernel", ctypes.c_int32), ("bwd_path", ctypes.c_int32),
+                ("bwd_tile_rows", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 @dataclass
 class Desc:
-    """Shard [s_local, b, h] of rank shard_index of t, and region settings."""
+    """Shard [s_local, b, h] of rank shard_index of t, region settings, and
+    the launch choices (0: the library's own)."""
     s_local: int
     b: int
     h: int
@@ -46,6 +51,9 @@ class Desc:
     eps: float = 1e-5
     seed: int = 0
     offset: int = 0
+    fwd_kernel: int = SPR_FWD_AUTO
+    bwd_path: int = SPR_BWD_AUTO
+    bwd_tile_rows: int = 0
 
     @property
     def rows(self):
@@ -53,13 +61,14 @@ class Desc:
 
     def c(self):
         return spr_desc(self.s_local, self.b, self.h, self.shard_index, self.t, self.io,
-                        self.norm, self.p, self.eps, self.seed, self.offset)
+                        self.norm, self.p, self.eps, self.seed, self.offset, self.fwd_kernel,
+                        self.bwd_path, self.bwd_tile_rows, 0)
 
 
 class spr_attn_desc(ctypes.Structure):
     _fields_ = [("s_local", ctypes.c_int64), ("b", ctypes.c_int64), ("heads", ctypes.c_int32),
                 ("d", ctypes.c_int32), ("t", ctypes.c_int32), ("rank", ctypes.c_int32),
-                ("scale", ctypes.c_float)]
+                ("scale", ctypes.c_float), ("steps_per_wg", ctypes.c_int32)]
 
 
 @dataclass
@@ -72,6 +81,7 @@ class AttnDesc:
     t: int = 1
     rank: int = 0
     scale: float = 0.0
+    steps_per_wg: int = 0       # launch choice: 0 = the library's own, else a divisor of t
 
     @property
     def rows(self):
@@ -79,7 +89,7 @@ class AttnDesc:
 
     def c(self):
         return spr_attn_desc(self.s_local, self.b, self.heads, self.d, self.t, self.rank,
-                             self.scale)
+                             self.scale, self.steps_per_wg)
 
 
 _lib = None
@@ -370,7 +380,8 @@ def alloc_fwd_outputs(d, device, store_mask=True, norm=True, write_h=True):
 
 
 def alloc_bwd_outputs(d, device, want_dbias=True):
-    """torch.empty outputs of sp_region_bwd and a zero-filled workspace."""
+    """torch.empty outputs of sp_region_bwd and its workspace (whose contents
+    on entry do not matter)."""
     import torch
     N, H, io = d.rows, d.h, _io_dtype(d)
     e = lambda n, dt: torch.empty(n, dtype=dt, device=device)
@@ -378,7 +389,7 @@ def alloc_bwd_outputs(d, device, want_dbias=True):
     return {"dx": e(N * H, io), "dres": e(N * H, io), "dgamma": e(H, torch.float32),
             "dbeta": e(H, torch.float32) if d.norm == SPR_LAYERNORM else None,
             "dbias": e(H, torch.float32) if want_dbias else None,
-            "workspace": torch.zeros(ws, dtype=torch.uint8, device=device)}
+            "workspace": e(ws, torch.uint8)}
 
 
 def fwd(d, x, bias, residual, gamma, beta, stream=None, store_mask=True, write_h=True):

@@ -34,15 +34,17 @@ def flags():
             "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC]
 
 
-def build(out=LIB, verbose=False):
-    """Compiles every source in parallel, links the shared library, returns its path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(out=LIB, verbose=False, extra=(), build_dir=BUILD_DIR):
+    """Compiles every source in parallel, links the shared library, returns its
+    path.  `extra` flags go on every compile and on the link (e.g. host-only
+    sanitizers: -Xarch_host -fsanitize=...)."""
+    os.makedirs(build_dir, exist_ok=True)
     cc = hipcc()
     objs, procs = [], []
     for src in SOURCES:
-        obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
+        obj = os.path.join(build_dir, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmd = [cc, *flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *flags(), *extra, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
@@ -57,7 +59,7 @@ def build(out=LIB, verbose=False):
     if failed:
         raise RuntimeError("hipcc failed:\n" + "\n".join(f"--- {s}\n{t}" for s, t in failed))
     tmp = out + ".tmp"
-    subprocess.run([cc, "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs], check=True)
+    subprocess.run([cc, "-shared", f"--offload-arch={ARCH}", *extra, "-o", tmp, *objs], check=True)
     os.replace(tmp, out)
     return out
 

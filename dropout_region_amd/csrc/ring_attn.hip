@@ -33,10 +33,10 @@
 #include <math.h>
 
 #include <atomic>
-#include <cstdlib>
 
 #include "sp_device.h"
 #include "sp_host_checks.h"
+#include "sp_plan.h"
 #include "sp_ring_attn.h"
 
 namespace spr {
@@ -447,6 +447,8 @@ bool attn_desc_ok(const spr_attn_desc* d) {
     if (d->d != 64 && d->d != 128) return false;
     if (d->b * (int64_t)d->heads > 65535) return false;
     if (!(d->scale >= 0.0f) || isinf(d->scale)) return false;               // also NaN
+    if (d->steps_per_wg < 0 || d->steps_per_wg > d->t) return false;
+    if (d->steps_per_wg > 0 && d->t % d->steps_per_wg != 0) return false;
     // every index (t blocks of s_local*b*heads*d elements) well inside 63 bits
     if ((double)d->t * (double)d->s_local * (double)d->b * d->heads * d->d > 4.0e18) return false;
     // all steps' query tiles in one launch dimension
@@ -470,18 +472,14 @@ uint64_t workspace_need(const spr_attn_desc* d) {
 // walks a longer run of key tiles and the merge folds t / k partials instead
 // of t (measured on MI355X, 4096 queries x 32768 keys, t = 8, the whole
 // fused call: 4 steps per workgroup 549 us, 2: 565, 1: 600, 8 -- half the
-// CUs idle -- 924).  SPR_ATTN_STEPS_PER_WG=k asks for k (a divisor of t;
-// tests check several).
+// CUs idle -- 924).  desc.steps_per_wg = k asks for k (a divisor of t).
 int steps_per_workgroup(const spr_attn_desc* d) {
-    const char* env = getenv("SPR_ATTN_STEPS_PER_WG");
-    if (env) {
-        const int k = atoi(env);
-        if (k >= 1 && d->t % k == 0) return k;
-    }
+    if (d->steps_per_wg > 0) return d->steps_per_wg;
     const int64_t per_step = (d->s_local + 32 * kWaves - 1) / (32 * kWaves) * d->b * d->heads;
+    const int64_t cus = device_cu_count();
     int spg = 1;
     for (int k = 2; k <= d->t; ++k)
-        if (d->t % k == 0 && per_step * (d->t / k) >= 256) spg = k;
+        if (d->t % k == 0 && per_step * (d->t / k) >= cus) spg = k;
     return spg;
 }
 

@@ -589,7 +589,7 @@ hipError_t launch_bwd_exit(const spr_desc& d, const BwdPlan& p, const BwdArgs& a
 // that the finalize reads back.
 int64_t bwd_teams(const spr_desc& d, const RowPlan& p) {
     const int64_t rows = d.s_local * d.b;
-    const int64_t cap = 256 * (int64_t)p.rpw;       // one workgroup per CU
+    const int64_t cap = (int64_t)device_cu_count() * p.rpw;   // one workgroup per CU
     const int64_t want = rows < cap ? rows : cap;
     return ((want + p.rpw - 1) / p.rpw) * p.rpw;
 }

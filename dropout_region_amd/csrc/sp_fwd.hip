@@ -15,8 +15,6 @@
 // h is bit-exact: u, v and h are each a single fp32 operation rounded to
 // nearest even (no contraction into FMA), then rounded to the I/O type.
 #include <atomic>
-#include <cstdlib>
-#include <cstring>
 
 #include "sp_device.h"
 #include "sp_plan.h"
@@ -433,47 +431,36 @@ static hipError_t fwd_by_norm(const spr_desc& d, const RowPlan& p, const FwdArgs
 }
 
 // ---------------------------------------------------------------- stream kernel dispatch
-static hipError_t cu_count(int* cus) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    e = hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (*cus < 1) *cus = 1;
-    return e;
-}
-
-// Workgroups of the stream kernel: per CU, enough for at least 8 waves (as
+// Workgroups of a stream kernel: per CU, enough for at least 8 waves (as
 // many as fit, if fewer), then trimmed so that every workgroup gets the same
-// number of rows (or one fewer).
-template <typename K>
-static hipError_t stream_grid(K kernel, int block, int64_t rows, int cus, int64_t* grid) {
-    static std::atomic<int> fit{0};       // workgroups of this kernel that fit on a CU
-    int occ = fit.load(std::memory_order_relaxed);
-    if (occ == 0) {
-        const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, block, 0);
-        if (e != hipSuccess) return e;
-        if (occ < 1) occ = 1;
-        fit.store(occ, std::memory_order_relaxed);
-    }
+// number of rows (or one fewer).  `occ` is how many of its workgroups fit on
+// a CU.
+static int64_t stream_grid(int occ, int block, int64_t rows, int cus) {
     const int waves = (block + 63) / 64;
     int per_cu = (8 + waves - 1) / waves;
     if (per_cu > occ) per_cu = occ;
     const int64_t cap = (int64_t)per_cu * cus;
     const int64_t per_wg = (rows + cap - 1) / cap;
-    *grid = (rows + per_wg - 1) / per_wg;
-    return hipSuccess;
+    return (rows + per_wg - 1) / per_wg;
 }
 
 template <typename IO, int NORM, bool DROP, int V, bool EXACT>
 static hipError_t fwd_stream_launch(const RowPlan& p, const FwdArgs& a, hipStream_t s) {
     constexpr int LB = stream_bound(Vec<IO>::N, V);
     auto kernel = sp_region_fwd_stream_kernel<IO, NORM, DROP, V, LB, EXACT>;
-    int cus = 0;
-    hipError_t e = cu_count(&cus);
-    if (e != hipSuccess) return e;
-    int64_t grid = 0;
-    e = stream_grid(kernel, p.block, a.rows, cus, &grid);
-    if (e != hipSuccess) return e;
+    // Workgroups of this instantiation that fit on a CU, kept with the block
+    // size they were queried for; a launch with another block size queries
+    // again.
+    static std::atomic<int64_t> fit{0};     // (block << 32) | occupancy
+    const int64_t f = fit.load(std::memory_order_relaxed);
+    int occ = (f >> 32) == p.block ? (int)(f & 0xffffffff) : 0;
+    if (occ == 0) {
+        const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, p.block, 0);
+        if (e != hipSuccess) return e;
+        if (occ < 1) occ = 1;
+        fit.store(((int64_t)p.block << 32) | occ, std::memory_order_relaxed);
+    }
+    const int64_t grid = stream_grid(occ, p.block, a.rows, device_cu_count());
     hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3((unsigned)p.block), 0, s, a);
     return hipGetLastError();
 }
@@ -517,15 +504,13 @@ static hipError_t fwd_stream_by_norm(const spr_desc& d, const RowPlan& p, const 
 
 // The row kernel by default.  The stream kernel (where its plan exists: at
 // most 16 elements per thread, so bias, gamma and beta fit in registers next
-// to two row buffers) runs when SPR_FWD_PATH=stream asks for it; measured on
+// to two row buffers) runs when desc.fwd_kernel asks for it; measured on
 // MI355X it is no faster anywhere the row kernel takes its preferred split
 // (long-sequence shard [4096, 1, 8192]: row kernel 59.2 us against 60.7 at
-// p = 0.1, 51.1 against 53.8 at p = 0).  SPR_FWD_PATH=rows|stream asks for
-// one kernel (tests check both).
+// p = 0.1, 51.1 against 53.8 at p = 0).
 hipError_t launch_fwd(const spr_desc& d, const RowPlan& p, const FwdArgs& a, hipStream_t s) {
     RowPlan sp;
-    const char* force = getenv("SPR_FWD_PATH");
-    bool stream = force && strcmp(force, "stream") == 0 && make_stream_plan(d.io, d.h, &sp);
+    bool stream = d.fwd_kernel == SPR_FWD_STREAM && make_stream_plan(d.io, d.h, &sp);
     if (a.nparts > 1) stream = false;    // the prologue is in the row kernel only
     if (stream)
         return d.io == SPR_BF16 ? fwd_stream_by_norm<__bf16>(d, sp, a, s)

@@ -151,6 +151,12 @@ struct BwdPlan {
 
 bool make_bwd_plan(const spr_desc& d, BwdPlan* plan);
 
+// Compute units of the current device, queried once per device and kept
+// (a launch fact, like an occupancy).  Where no device can be queried (a
+// process without a GPU sizing a workspace) it is the 256 of a whole
+// MI355X, the chip this library is built for.
+int device_cu_count();
+
 // Kernel launches of the backward for this plan (fused: rows, finalize;
 // split: rowsum, main, finalize).
 int bwd_num_launches(const BwdPlan& plan);

@@ -3,8 +3,8 @@
 // HIP call, so an invalid call launches nothing and touches no output.
 #include <math.h>
 #include <stdint.h>
-#include <stdlib.h>
-#include <string.h>
+
+#include <atomic>
 
 #include "sp_host_checks.h"
 #include "sp_plan.h"
@@ -118,13 +118,33 @@ bool make_stream_plan(int io, int64_t h, RowPlan* plan) {
     return true;
 }
 
+int device_cu_count() {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cus[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    int n = cus[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n < 1) {
+            (void)hipGetLastError();
+            n = 256;
+        }
+        cus[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
 static size_t round256(uint64_t b) { return (size_t)((b + 255u) & ~(uint64_t)255u); }
 
 // Chooses the backward path: fused whenever its row team fits in registers
 // (at most two vectors per thread), split otherwise -- measured on MI355X,
 // the fused path is the faster one wherever it applies, even on shards where
 // its partial rows outweigh the split path's second read of dy and h.
-// SPR_BWD_PATH=fused|split asks for one path (tests check both).
+// desc.bwd_path asks for one path, desc.bwd_tile_rows for a tile height.
 bool make_bwd_plan(const spr_desc& d, BwdPlan* plan) {
     BwdPlan p{};
     if (!make_row_plan(d.io, d.h, kPlanBackward, &p.rows)) return false;
@@ -142,14 +162,10 @@ bool make_bwd_plan(const spr_desc& d, BwdPlan* plan) {
     // against about one tile per CU: split second pass + finalize 61.6 ->
     // 47.7 us on the 175B shard, 358 -> 328 us on the 1T t = 1 shard; exit
     // 33.4 -> 27.4 us (175B), 194 -> 176 us (1T t = 1).
-    // SPR_BWD_TILE_ROWS=n (a multiple of 16) overrides both.
+    // desc.bwd_tile_rows (a multiple of 16) overrides both.
     const int64_t rows16 = (rows + 15) / 16 * 16;
     int64_t tr = 32, tr_exit = 16;
-    const char* trs = getenv("SPR_BWD_TILE_ROWS");
-    if (trs) {
-        const long v = strtol(trs, nullptr, 10);
-        if (v >= 16 && v % 16 == 0 && v <= (1L << 20)) tr = tr_exit = v;
-    }
+    if (d.bwd_tile_rows > 0) tr = tr_exit = d.bwd_tile_rows;
     // The row blocks are the grid's y dimension, at most 65535.
     const int64_t min_tr = ((rows + 65534) / 65535 + 15) / 16 * 16;
     if (tr < min_tr) tr = min_tr;
@@ -170,9 +186,7 @@ bool make_bwd_plan(const spr_desc& d, BwdPlan* plan) {
     p.workspace = round256(ws);
 
     p.path = fused_ok ? kBwdFused : kBwdSplit;
-    const char* force = getenv("SPR_BWD_PATH");
-    if (force && strcmp(force, "split") == 0) p.path = kBwdSplit;
-    if (force && strcmp(force, "fused") == 0 && fused_ok) p.path = kBwdFused;
+    if (d.bwd_path == SPR_BWD_SPLIT) p.path = kBwdSplit;
     *plan = p;
     return true;
 }
@@ -192,6 +206,12 @@ spr_status check_fields(const spr_desc* d) {
     if (d->norm != SPR_LAYERNORM && d->norm != SPR_RMSNORM) return SPR_ERR_INVALID_ARG;
     if (!(d->p >= 0.0f && d->p < 1.0f)) return SPR_ERR_INVALID_ARG;      // also rejects NaN
     if (!(d->eps > 0.0f) || isinf(d->eps)) return SPR_ERR_INVALID_ARG;
+    if (d->fwd_kernel < SPR_FWD_AUTO || d->fwd_kernel > SPR_FWD_STREAM) return SPR_ERR_INVALID_ARG;
+    if (d->bwd_path < SPR_BWD_AUTO || d->bwd_path > SPR_BWD_SPLIT) return SPR_ERR_INVALID_ARG;
+    if (d->bwd_tile_rows != 0 &&
+        (d->bwd_tile_rows < 16 || d->bwd_tile_rows % 16 != 0 || d->bwd_tile_rows > (1 << 20)))
+        return SPR_ERR_INVALID_ARG;
+    if (d->reserved != 0) return SPR_ERR_INVALID_ARG;
     // N*h and the global element index (t*N*h) must fit comfortably in 63 bits.
     if (d->s_local > (INT64_C(1) << 40) / d->b) return SPR_ERR_UNSUPPORTED;
     const int64_t rows = d->s_local * d->b;
@@ -275,7 +295,7 @@ spr_status fwd_impl(const spr_desc* d, const void* x, int nparts, const float* b
 
 extern "C" {
 
-const char* sp_region_status_string(spr_status s) {
+const char* sp_region_status_string(int s) {
     switch (s) {
         case SPR_OK: return "ok";
         case SPR_ERR_INVALID_ARG: return "invalid argument";

@@ -60,10 +60,11 @@
  *  - Calls are asynchronous on `stream` (NULL = the null stream): they
  *    return after the launches and the outputs are valid once the stream
  *    has reached that point.
- *  - Errors: every argument is checked on the host before any HIP call; on
- *    an error nothing is launched and no output is touched.  SPR_ERR_HIP
- *    means a HIP call failed (the HIP error is consumed); outputs are then
- *    undefined.
+ *  - Errors: every argument is checked on the host before anything is
+ *    launched (only device queries -- the compute-unit count, a kernel's
+ *    occupancy -- may run first); on an error nothing is launched and no
+ *    output is touched.  SPR_ERR_HIP means a HIP call failed (the HIP error
+ *    is consumed); outputs are then undefined.
  */
 #ifndef SP_REGION_H
 #define SP_REGION_H
@@ -101,7 +102,28 @@ typedef struct {
     float    eps;          /* > 0, finite                                           */
     uint64_t seed;         /* dropout key                                           */
     uint64_t offset;       /* dropout stream, one per dropout site (e.g. 2*layer+k) */
+    /* Launch choices; 0 everywhere = the library's own (the usual setting).
+     * They select which kernels run, never what is computed: masks and h are
+     * the same bits under every choice, the rest meets the same tolerances,
+     * and every choice is deterministic.  Out-of-range values are
+     * SPR_ERR_INVALID_ARG. */
+    int32_t  fwd_kernel;     /* SPR_FWD_AUTO, SPR_FWD_ROWS (one team per row), or
+                                SPR_FWD_STREAM (a chip-filling grid walking rows;
+                                where it has no plan -- rows of <= 2048 bf16 / 1024
+                                fp32 elements or > 16 elements per thread -- and in
+                                sp_region_fwd_rs the row kernel runs)            */
+    int32_t  bwd_path;       /* SPR_BWD_AUTO, SPR_BWD_FUSED (one row pass, where a
+                                row team's column sums fit in registers; else the
+                                split passes run), or SPR_BWD_SPLIT (a row-sum pass,
+                                then column tiles)                               */
+    int32_t  bwd_tile_rows;  /* 0, or rows per tile of the split backward's second
+                                pass and of sp_region_bwd_exit: a multiple of 16 in
+                                [16, 2^20] (raised to fit 65535 row blocks)      */
+    int32_t  reserved;       /* must be 0                                        */
 } spr_desc;
+
+enum { SPR_FWD_AUTO = 0, SPR_FWD_ROWS = 1, SPR_FWD_STREAM = 2 };
+enum { SPR_BWD_AUTO = 0, SPR_BWD_FUSED = 1, SPR_BWD_SPLIT = 2 };
 
 /* Forward of the region on one shard.
  *  x        [N,h] io   the reduce-scattered row-parallel output
@@ -169,9 +191,11 @@ spr_status sp_region_fwd_rs(const spr_desc* desc, const void* x_parts, int32_t n
                             float* mean_out, float* rstd_out,
                             hipStream_t stream);
 
-/* Bytes of device workspace sp_region_bwd needs for this desc (fp32
- * column partials of dgamma/dbeta/dbias and the kernels' coordination
- * words).  0 on an invalid desc. */
+/* Bytes of device workspace sp_region_bwd needs for this desc on the
+ * current device: fp32 column partials of dgamma/dbeta/dbias (one row of
+ * 3*h per row team, as many teams as the device has compute units, or per
+ * row tile of the split path) and the split path's per-row sums.  0 on an
+ * invalid desc. */
 size_t sp_region_bwd_workspace_bytes(const spr_desc* desc);
 
 /* Backward of the region on one shard, from the forward's saved tensors.
@@ -190,10 +214,10 @@ size_t sp_region_bwd_workspace_bytes(const spr_desc* desc);
  *  dgamma_out  [h]  fp32  this shard's partial sum over its N rows
  *  dbeta_out   [h]  fp32  LayerNorm: required; RMSNorm: must be NULL
  *  dbias_out   [h]  fp32  may be NULL (not computed)
- *  workspace   device memory of at least sp_region_bwd_workspace_bytes;
- *              it must be zero-filled before its first use with this
- *              library, and every call leaves it ready for the next one.
- *              Concurrent calls must use different workspaces.
+ *  workspace   device memory of at least sp_region_bwd_workspace_bytes,
+ *              16-byte aligned; its contents on entry do not matter (every
+ *              byte the call reads it writes first) and are undefined
+ *              after.  Concurrent calls must use different workspaces.
  * The parameter gradients are this shard's partial sums; adding them over
  * the t shards (a tensor-parallel all-reduce) is the caller's.  The
  * reductions run in a fixed order: two identical calls give identical bits. */
@@ -253,8 +277,9 @@ spr_status sp_region_bwd_launch(const spr_desc* desc, int index,
 spr_status sp_region_activation_bytes(const spr_desc* desc, uint64_t* saved_for_bwd,
                                       uint64_t* retained_output);
 
-/* Static description of a status code. */
-const char* sp_region_status_string(spr_status status);
+/* Static description of a status code (any int; values that are no
+ * spr_status give "unknown status"). */
+const char* sp_region_status_string(int status);
 
 #ifdef __cplusplus
 }

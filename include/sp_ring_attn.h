@@ -51,6 +51,12 @@ typedef struct {
     int32_t t;         /* ring size, the context-parallel degree (1 .. 65535)    */
     int32_t rank;      /* this rank, 0 <= rank < t: owns query block `rank`      */
     float   scale;     /* softmax scale; 0 means 1/sqrt(d)                       */
+    int32_t steps_per_wg;  /* launch choice for sp_ring_attn_fwd: 0 = the
+                              library's own, else k, a divisor of t: each
+                              workgroup walks k consecutive ring steps as one
+                              run of key tiles and the merge folds t/k
+                              partials (same results within the tolerance,
+                              deterministic for each k)                      */
 } spr_attn_desc;
 /* Also rejected (SPR_ERR_INVALID_ARG): ceil(s_local/256) * b * heads * t above
  * 2^31 - 1 (the 256-query tiles of all steps form one launch). */

@@ -20,6 +20,8 @@ Recipe (the pages measure on no dataset; activations are synthetic by nature):
   unit variance of x.
   Ring attention (make_attn_inputs): default_rng(seed + 2) draws q, then k
   and v of all t blocks, standard normals rounded to bf16.
+  The matched-key attention inputs (make_attn_inputs_matched) come from
+  default_rng(seed + 4); see that function.
 """
 from dataclasses import dataclass, field
 
@@ -97,6 +99,29 @@ def make_attn_inputs_ramp(s_local, b, heads, d, t, seed=0, span=200.0, rising=Tr
     v = rng.standard_normal(t * n)
     f = lambda a: to_bf16_bits(np.asarray(a, dtype=np.float32).reshape(-1))
     return {"q": f(q), "k": f(k), "v": f(v)}
+
+
+def make_attn_inputs_matched(s_local, b, heads, d, t, seed=0, gain=4.0):
+    """Ring attention in which every query has one key of its own that
+    dominates its softmax: q is standard normal (rounded to bf16), every key
+    starts as 0.5 N(0,1) and value as N(0,1); then, per (batch, head), query i
+    is matched to key perm[i] (a random injection of the s_local queries into
+    the t * s_local keys) and that key is set to gain * q_i (gain a power of
+    two, so exact in bf16).  The matched score, gain |q_i|^2 / sqrt(d) ~
+    gain sqrt(d), exceeds every other by ~20 or more, so the output is the
+    matched key's value to within ~1e-6: a value read from the wrong key
+    position moves it by O(1).  Drawn from default_rng(seed + 4) in the order
+    q, k, v, perm, as bf16 bits."""
+    rng = np.random.default_rng(seed + 4)
+    S, T = s_local, t * s_local
+    q = to_bf16_bits(rng.standard_normal((S, b, heads, d), dtype=np.float32))
+    k = rng.standard_normal((T, b, heads, d), dtype=np.float32) * np.float32(0.5)
+    v = rng.standard_normal(T * b * heads * d, dtype=np.float32)
+    perm = rng.permutation(T)[:S]
+    qf = (q.astype(np.uint32) << 16).view(np.float32)
+    k[perm] = np.float32(gain) * qf
+    return {"q": q.reshape(-1), "k": to_bf16_bits(k.reshape(-1)), "v": to_bf16_bits(v),
+            "perm": perm}
 
 
 @dataclass

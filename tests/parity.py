@@ -11,9 +11,6 @@ accumulation on the GPU and float64 in the oracle:
   dgamma, dbeta, dbias (fp32): max|a - b| / max|b| <= 1e-4
 ulp_bf16(b) = 2^(floor(log2 |b|) - 7), the spacing of bfloat16 at b.
 """
-import contextlib
-import os
-
 import numpy as np
 
 F32, BF16 = 0, 1
@@ -141,35 +138,36 @@ def oracle_bwd(od, inp, saved, with_dh_out=False, want_dbias=True):
                       want_dbias=want_dbias)
 
 
-@contextlib.contextmanager
-def _env(name, value):
-    """Sets environment variable `name` to `value` (None: leave it alone)
-    for the duration of the block."""
-    old = os.environ.get(name)
-    if value is not None:
-        os.environ[name] = value
-    try:
-        yield
-    finally:
-        if value is not None:
-            if old is None:
-                del os.environ[name]
-            else:
-                os.environ[name] = old
+_FWD = {None: 0, "rows": 1, "stream": 2}
+_BWD = {None: 0, "fused": 1, "split": 2}
+
+
+def tuned(d, fwd=None, bwd=None, tile_rows=None):
+    """d with the launch choices set: fwd = "rows" or "stream" (forward
+    kernel), bwd = "fused" or "split" (backward path), tile_rows (split and
+    exit tiles); None leaves a choice to the library."""
+    import dataclasses
+    kw = {}
+    if fwd is not None:
+        kw["fwd_kernel"] = _FWD[fwd]
+    if bwd is not None:
+        kw["bwd_path"] = _BWD[bwd]
+    if tile_rows is not None:
+        kw["bwd_tile_rows"] = int(tile_rows)
+    return dataclasses.replace(d, **kw) if kw else d
 
 
 def gpu_fwd(d, inp, with_bias=True, device="cuda:0", path=None, store_mask=True):
     """Forward on the GPU; path = "rows" or "stream" asks the library for
-    that forward kernel (SPR_FWD_PATH), None for its own choice.
+    that forward kernel, None for its own choice.
     store_mask=False: no mask is stored (the backward regenerates it)."""
     import dropout_region_amd as spr
     io = d.io
-    with _env("SPR_FWD_PATH", path):
-        o = spr.fwd(d, to_device(inp["x"], io, device),
-                    to_device(inp["bias"], device=device) if with_bias else None,
-                    to_device(inp["residual"], io, device), to_device(inp["gamma"], device=device),
-                    to_device(inp["beta"], device=device) if d.norm == 0 else None,
-                    store_mask=store_mask)
+    o = spr.fwd(tuned(d, fwd=path), to_device(inp["x"], io, device),
+                to_device(inp["bias"], device=device) if with_bias else None,
+                to_device(inp["residual"], io, device), to_device(inp["gamma"], device=device),
+                to_device(inp["beta"], device=device) if d.norm == 0 else None,
+                store_mask=store_mask)
     return {k: to_host(v) for k, v in o.items()}
 
 
@@ -189,10 +187,9 @@ def gpu_bwd(d, inp, saved, with_dh_out=False, want_dbias=True, device="cuda:0", 
     """Backward from `saved` (host arrays of h, mask, mean, rstd).  With
     repeat > 1 the call is made that many times into the same outputs and
     workspace, and every result must be bit-identical.  path = "fused" or
-    "split" asks the library for that backward path (SPR_BWD_PATH)."""
+    "split" asks the library for that backward path."""
     import dropout_region_amd as spr
-    with _env("SPR_BWD_PATH", path):
-        return _gpu_bwd(spr, d, inp, saved, with_dh_out, want_dbias, device, repeat)
+    return _gpu_bwd(spr, tuned(d, bwd=path), inp, saved, with_dh_out, want_dbias, device, repeat)
 
 
 def _gpu_bwd(spr, d, inp, saved, with_dh_out, want_dbias, device, repeat):

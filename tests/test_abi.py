@@ -77,10 +77,30 @@ FWD_OK = [A, A + 0x100000, A + 0x200000, A + 0x300000, A + 0x310000, A + 0x40000
     ("h", 0, spr.SPR_ERR_INVALID_ARG), ("s_local", 0, spr.SPR_ERR_INVALID_ARG),
     ("io", 5, spr.SPR_ERR_INVALID_ARG), ("norm", 2, spr.SPR_ERR_INVALID_ARG),
     ("h", 60, spr.SPR_ERR_UNSUPPORTED), ("h", 32776, spr.SPR_ERR_UNSUPPORTED),
+    ("fwd_kernel", 3, spr.SPR_ERR_INVALID_ARG), ("fwd_kernel", -1, spr.SPR_ERR_INVALID_ARG),
+    ("bwd_path", 3, spr.SPR_ERR_INVALID_ARG), ("bwd_tile_rows", 8, spr.SPR_ERR_INVALID_ARG),
+    ("bwd_tile_rows", 40, spr.SPR_ERR_INVALID_ARG),
+    ("bwd_tile_rows", 2 ** 21, spr.SPR_ERR_INVALID_ARG),
 ])
 def test_fwd_rejects_bad_desc(L, field, value, status):
     d = _good_desc(**{field: value})
     assert _fwd_raw(L, d, FWD_OK) == status
+
+
+def test_launch_choices_are_checked_by_every_entry_point(L):
+    """A nonzero reserved word, or a launch choice out of range, is an
+    invalid descriptor for the backward and its workspace query too."""
+    for bad in (dict(bwd_path=-2), dict(bwd_tile_rows=24)):
+        d = _good_desc(**bad)
+        assert L.sp_region_bwd_workspace_bytes(ctypes.byref(d)) == 0, bad
+        assert L.sp_region_bwd_num_launches(ctypes.byref(d)) == 0, bad
+    d = _good_desc()
+    d.reserved = 1
+    assert _fwd_raw(L, d, FWD_OK) == spr.SPR_ERR_INVALID_ARG
+    assert L.sp_region_bwd_workspace_bytes(ctypes.byref(d)) == 0
+    for ok in (dict(fwd_kernel=spr.SPR_FWD_STREAM), dict(bwd_path=spr.SPR_BWD_SPLIT),
+               dict(bwd_tile_rows=48)):
+        assert L.sp_region_bwd_workspace_bytes(ctypes.byref(_good_desc(**ok))) > 0, ok
 
 
 def _fwd_rs_raw(L, d, nparts, ptrs):
@@ -206,7 +226,8 @@ def test_ring_attn_rejects_bad_calls(L):
         return spr.AttnDesc(**base).c()
     assert L.sp_ring_attn_workspace_bytes(ctypes.byref(desc())) > 0
     for bad in (dict(d=96), dict(rank=4), dict(rank=-1), dict(t=0), dict(s_local=0),
-                dict(heads=70000), dict(scale=float("nan")), dict(scale=-1.0)):
+                dict(heads=70000), dict(scale=float("nan")), dict(scale=-1.0),
+                dict(steps_per_wg=3), dict(steps_per_wg=8), dict(steps_per_wg=-1)):
         d = desc(**bad)
         assert L.sp_ring_attn_workspace_bytes(ctypes.byref(d)) == 0, bad
         assert L.sp_ring_attn_fwd(ctypes.byref(d), *[ctypes.c_void_p(A + i * 0x1000000) for i in range(5)],

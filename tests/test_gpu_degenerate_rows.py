@@ -3,12 +3,13 @@
 * Constant rows (every h of the row equal): the variance is 0, so
   rstd = 1/sqrt(eps) and y = beta (LayerNorm) or sign(h) * gamma / sqrt(1 +
   eps/h^2) (RMSNorm); the backward sees xhat = 0 and a large rstd.
-* fp32 rows whose mean is 10^4 times their spread: a one-pass variance
-  (E[h^2] - E[h]^2 in fp32) would lose every digit here; the statistics must
-  still meet the 1e-5 relative tolerance.  y is compared within a bound that
-  follows from the arithmetic: rounding the mean itself to fp32 moves it by
-  up to ulp(mean)/2, which moves y by that times rstd, so
-  |y - y_ref| <= 8 * ulp_fp32(mean) * rstd + 1e-5.
+* fp32 rows whose mean is 10^3-10^4 times their spread: a one-pass variance
+  (E[h^2] - E[h]^2 in fp32) would lose every digit here.  The statistics
+  must meet the 1e-5 relative tolerance and y the fp32 1e-5 max-abs one,
+  like any other row: the kernel subtracts a pivot taken from the row before
+  it forms any sum, so no fp32 number of the size of the mean ever enters
+  the normalised value ((h - pivot) - mean_rel) * rstd.  The backward on the
+  same rows (both paths) must meet the usual gradient tolerances.
 """
 import zlib
 
@@ -83,16 +84,12 @@ def test_large_mean_rows_fp32(h, mean):
     inp["residual"] = (np.float32(mean) + inp["residual"]).astype(np.float32)
     inp["x"] = (np.float32(0.1) * inp["x"]).astype(np.float32)
     want = P.oracle_fwd(od, inp)
-    ulp_mean = 2.0 ** (np.floor(np.log2(abs(mean))) - 23)
     for path in (None, "rows", "stream"):
         got = P.gpu_fwd(d, inp, path=path)
-        P.exact("mask", got["mask"], want["mask"])
-        P.exact("h", got["h"], want["h"])
-        P.stats_close("mean", got["mean"], want["mean"])
-        P.stats_close("rstd", got["rstd"], want["rstd"])
-        rstd = np.repeat(np.asarray(want["rstd"], np.float64), d.h)
-        err = np.abs(got["y"].astype(np.float64) - want["y"].astype(np.float64))
-        bound = 8.0 * ulp_mean * rstd + 1e-5
-        bad = np.flatnonzero(err > bound)
-        assert bad.size == 0, (f"y ({path}): {bad.size} outside; first at {bad[0]}: "
-                               f"{got['y'][bad[0]]} vs {want['y'][bad[0]]}")
+        _say(f"[case] large-mean rows, forward kernel {path or 'auto'}")
+        P.check_fwd(got, want, d.io)
+    wb = P.oracle_bwd(od, inp, want, want_dbias=True)
+    for path in ("fused", "split"):
+        _say(f"[case] large-mean rows, backward path {path}")
+        gb = P.gpu_bwd(d, inp, want, want_dbias=True, repeat=2, path=path)
+        P.check_bwd(gb, wb, d.io)

@@ -44,20 +44,20 @@ def test_graph_replays_equal_eager(h, rows, fwd_path, bwd_path):
          "dy": P.to_device(inp["dy"], d.io), "dh_out": P.to_device(inp["dh_out"], d.io),
          "bias": P.to_device(inp["bias"]), "gamma": P.to_device(inp["gamma"]),
          "beta": P.to_device(inp["beta"])}
-    with P._env("SPR_FWD_PATH", fwd_path), P._env("SPR_BWD_PATH", bwd_path):
-        eager = _outputs(d, dev)
-        _run(d, a, eager)
-        torch.cuda.synchronize()
-        want = {k: P.to_host(eager[k]) for k in _KEYS}
+    d = P.tuned(d, fwd=fwd_path, bwd=bwd_path)
+    eager = _outputs(d, dev)
+    _run(d, a, eager)
+    torch.cuda.synchronize()
+    want = {k: P.to_host(eager[k]) for k in _KEYS}
 
-        o = _outputs(d, dev)
-        g = torch.cuda.CUDAGraph()
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.graph(g, stream=side):
-            _run(d, a, o)
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
+    o = _outputs(d, dev)
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(g, stream=side):
+        _run(d, a, o)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
     for rep in range(3):
         for k in _KEYS:
             o[k].zero_()

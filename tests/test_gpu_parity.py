@@ -37,10 +37,12 @@ def descs(**kw):
 
 
 def run_case(name, kw, seed=0, with_bias=True, with_dh_out=False, want_dbias=True,
-             paths=(None,), fwd_paths=(None,)):
+             paths=(None,), fwd_paths=(None,), tile_rows=None):
     """paths: backward paths to check (None = the library's own choice,
-    "fused", "split"); fwd_paths: forward kernels (None, "rows", "stream")."""
+    "fused", "split"); fwd_paths: forward kernels (None, "rows", "stream");
+    tile_rows: rows per tile of the split backward (None: the library's)."""
     d, od = descs(**kw)
+    d = P.tuned(d, tile_rows=tile_rows)
     _say(f"[case] {name}: {kw} bias={with_bias} dh_out={with_dh_out} dbias={want_dbias}")
     inp = make_inputs(d.rows, d.h, d.io, seed=seed, dh_out=with_dh_out)
     want = P.oracle_fwd(od, inp, with_bias)
@@ -102,21 +104,19 @@ def test_small_shapes(name):
 # Rows per tile of the split path's second pass and of the exit (16 and 32
 # by default): other tilings must give results within the same tolerances,
 # on shapes whose last tile is ragged.
-@pytest.mark.parametrize("tile_rows", ["16", "48", "64"])
+@pytest.mark.parametrize("tile_rows", [16, 48, 64])
 def test_split_tile_rows(tile_rows):
-    with P._env("SPR_BWD_TILE_ROWS", tile_rows):
-        run_case(f"split tiles of {tile_rows} rows", base(s_local=1003, b=1, h=6144, offset=3),
-                 seed=11, with_dh_out=True, paths=("split",))
-        run_case(f"split tiles of {tile_rows} rows, fp32 RMS",
-                 base(s_local=37, b=3, h=3076, io=F32, norm=RMS, p=0.3), seed=12,
-                 paths=("split",))
+    run_case(f"split tiles of {tile_rows} rows", base(s_local=1003, b=1, h=6144, offset=3),
+             seed=11, with_dh_out=True, paths=("split",), tile_rows=tile_rows)
+    run_case(f"split tiles of {tile_rows} rows, fp32 RMS",
+             base(s_local=37, b=3, h=3076, io=F32, norm=RMS, p=0.3), seed=12,
+             paths=("split",), tile_rows=tile_rows)
 
 
-@pytest.mark.parametrize("tile_rows", ["32", "64"])
+@pytest.mark.parametrize("tile_rows", [32, 64])
 def test_norm_free_exit_tile_rows(tile_rows):
-    with P._env("SPR_BWD_TILE_ROWS", tile_rows):
-        test_norm_free_exit("bf16_h8192_1100_rows")
-        test_norm_free_exit("fp32_h260_ragged_p0.3")
+    test_norm_free_exit("bf16_h8192_1100_rows", tile_rows)
+    test_norm_free_exit("fp32_h260_ragged_p0.3", tile_rows)
 
 
 # Seeded random shapes: widths anywhere in the supported range (bf16: any
@@ -218,11 +218,10 @@ def test_reduce_scatter_prologue(name):
     parts = make_parts(d.rows, d.h, d.io, nparts, seed=seed)
     x = oracle.reduce_parts(od, parts)
     want = P.oracle_fwd(od, dict(inp, x=x))
-    # the row kernel on both sides (with one part, SPR_FWD_PATH=stream would
-    # otherwise send the prologue call to the stream kernel, whose reductions
-    # run in another order)
-    with P._env("SPR_FWD_PATH", "rows"):
-        got = P.gpu_fwd_rs(d, inp, parts, nparts)
+    # the row kernel on both sides (with one part, a stream-kernel choice
+    # would otherwise send the prologue call to the stream kernel, whose
+    # reductions run in another order)
+    got = P.gpu_fwd_rs(P.tuned(d, fwd="rows"), inp, parts, nparts)
     P.check_fwd(got, want, d.io)
     # bit-identical to the plain forward (same kernel) on the summed x
     plain = P.gpu_fwd(d, dict(inp, x=x), path="rows")
@@ -254,9 +253,8 @@ def test_norm_only_entry(name):
     res = P.to_device(inp["residual"], d.io)
     gam, bet = P.to_device(inp["gamma"]), P.to_device(inp["beta"]) if ln else None
     for fpath in (None, "rows", "stream"):
-        with P._env("SPR_FWD_PATH", fpath):
-            o = spr.fwd(d, None, None, res, gam, bet, write_h=False)
-            oh = spr.fwd(d, None, None, res, gam, bet, write_h=True)
+        o = spr.fwd(P.tuned(d, fwd=fpath), None, None, res, gam, bet, write_h=False)
+        oh = spr.fwd(P.tuned(d, fwd=fpath), None, None, res, gam, bet, write_h=True)
         got = {k: P.to_host(v) for k, v in o.items()}
         assert got["h"] is None and got["mask"] is None
         P.io_close("y", got["y"], want["y"], d.io)
@@ -270,13 +268,13 @@ def test_norm_only_entry(name):
     wb = oracle.bwd(od, inp["dy"], inp["dh_out"], inp["residual"], None, want["mean"],
                     want["rstd"], inp["gamma"], want_dbias=False, want_dx=False)
     for path in ("fused", "split"):
-        with P._env("SPR_BWD_PATH", path):
-            b = spr.alloc_bwd_outputs(d, res.device, want_dbias=False)
-            spr.sp_region_bwd(d, P.to_device(inp["dy"], d.io), P.to_device(inp["dh_out"], d.io),
-                              res, None, P.to_device(want["mean"]), P.to_device(want["rstd"]),
-                              gam, None, b["dres"], b["dgamma"], b["dbeta"], None,
-                              b["workspace"])
-            torch.cuda.synchronize()
+        dp = P.tuned(d, bwd=path)
+        b = spr.alloc_bwd_outputs(dp, res.device, want_dbias=False)
+        spr.sp_region_bwd(dp, P.to_device(inp["dy"], d.io), P.to_device(inp["dh_out"], d.io),
+                          res, None, P.to_device(want["mean"]), P.to_device(want["rstd"]),
+                          gam, None, b["dres"], b["dgamma"], b["dbeta"], None,
+                          b["workspace"])
+        torch.cuda.synchronize()
         P.io_close(f"dres ({path})", P.to_host(b["dres"]), wb["dres"], d.io)
         P.param_grad_close(f"dgamma ({path})", P.to_host(b["dgamma"]), wb["dgamma"])
         if ln:
@@ -294,17 +292,17 @@ EXIT = {
 
 
 @pytest.mark.parametrize("name", sorted(EXIT))
-def test_norm_free_exit(name):
+def test_norm_free_exit(name, tile_rows=None):
     import torch
     d, od = descs(**EXIT[name])
+    d = P.tuned(d, tile_rows=tile_rows)
     _say(f"[case] norm-free exit {name}: {EXIT[name]}")
     inp = make_inputs(d.rows, d.h, d.io, seed=zlib.crc32(name.encode()) % 1000, dh_out=True)
     want = oracle.fwd(od, inp["x"], inp["bias"], inp["residual"], None, None)
     x, res = P.to_device(inp["x"], d.io), P.to_device(inp["residual"], d.io)
     bias = P.to_device(inp["bias"])
     for fpath in (None, "rows", "stream"):
-        with P._env("SPR_FWD_PATH", fpath):
-            o = spr.fwd(d, x, bias, res, None, None)
+        o = spr.fwd(P.tuned(d, fwd=fpath), x, bias, res, None, None)
         got = {k: P.to_host(v) for k, v in o.items()}
         for k in ("y", "mean", "rstd"):
             assert got[k] is None
@@ -340,6 +338,56 @@ def test_optional_arguments(with_bias, with_dh_out, want_dbias, io, norm):
     kw = base(s_local=6, b=2, h=6144 if io == BF16 else 1024, io=io, norm=norm)
     run_case(f"optional io={io} norm={norm}", kw, seed=3, with_bias=with_bias,
              with_dh_out=with_dh_out, want_dbias=want_dbias, paths=("fused", "split"))
+
+
+def test_tiny_fp32_workload_as_specified():
+    """The tiny fp32 workload exactly as specified: the full [128, 2, 256]
+    tensor (seed 0, x, residual and the gradient of y standard normal, bias
+    and beta N(0, 0.02), gamma 1 + N(0, 0.02); LayerNorm eps 1e-5, p 0.1),
+    run unsharded (t = 1) and as both shards [64, 2, 256] of t = 2.  Each
+    run is checked element by element against the oracle; the two shards
+    concatenated equal the t = 1 run bit for bit (the band is per token:
+    "Sequence parallel math", section "The move: split the LayerNorm/dropout
+    band along the sequence"), and the shards' parameter gradients summed
+    equal the t = 1 ones within 1e-4."""
+    w = WORKLOADS["tiny_fp32_t2"]
+    full_kw = dict(s_local=w.s, b=w.b, h=w.h, shard_index=0, t=1, io=w.io, norm=w.norm, p=w.p,
+                   eps=w.eps, seed=w.seed, offset=0)
+    full, ofull = descs(**full_kw)
+    _say(f"[case] tiny fp32 workload, unsharded: {full_kw}")
+    inp = make_inputs(full.rows, w.h, w.io, seed=w.seed)
+    want = P.oracle_fwd(ofull, inp)
+    ref = P.gpu_fwd(full, inp)
+    P.check_fwd(ref, want, w.io)
+    wantb = P.oracle_bwd(ofull, inp, want)
+    refb = P.gpu_bwd(full, inp, ref, repeat=2)
+    P.check_bwd(refb, wantb, w.io)
+    N = w.rows
+    acc = {k: np.zeros(w.h) for k in ("dgamma", "dbeta", "dbias")}
+    for i in range(w.t):
+        kw = dict(full_kw, s_local=w.s_local, shard_index=i, t=w.t)
+        d, od = descs(**kw)
+        _say(f"[case] tiny fp32 workload, shard {i} of {w.t}: {kw}")
+        sl = slice(i * N * w.h, (i + 1) * N * w.h)
+        si = {k: (v[sl] if v is not None and v.size == full.rows * w.h else v)
+              for k, v in inp.items()}
+        ws = P.oracle_fwd(od, si)
+        o = P.gpu_fwd(d, si)
+        P.check_fwd(o, ws, w.io)
+        wbs = P.oracle_bwd(od, si, ws)
+        g = P.gpu_bwd(d, si, o, repeat=2)
+        P.check_bwd(g, wbs, w.io)
+        for k in ("h", "y", "mask"):
+            P.exact(f"{k} shard {i} vs t=1", o[k], ref[k][sl])
+            P.exact(f"oracle {k} shard {i} vs t=1", ws[k], want[k][sl])
+        for k in ("mean", "rstd"):
+            P.exact(f"{k} shard {i} vs t=1", o[k], ref[k][i * N:(i + 1) * N])
+        for k in ("dx", "dres"):
+            P.exact(f"{k} shard {i} vs t=1", g[k], refb[k][sl])
+        for k in acc:
+            acc[k] += g[k]
+    for k in acc:
+        P.param_grad_close(f"sum of shard {k} vs t=1", acc[k], refb[k])
 
 
 @pytest.mark.parametrize("io,h,t", [(F32, 256, 2), (BF16, 6144, 4), (BF16, 25600, 2)])
@@ -400,12 +448,12 @@ def test_workspace_and_argument_errors_leave_outputs_untouched():
 
 
 @pytest.mark.parametrize("path", ["fused", "split"])
-def test_launch_by_launch_equals_whole_backward(path, monkeypatch):
+def test_launch_by_launch_equals_whole_backward(path):
     """Running the backward's launches one at a time on the stream gives the
     same bits as sp_region_bwd."""
     import torch
-    monkeypatch.setenv("SPR_BWD_PATH", path)
     d, od = descs(**base(s_local=37, b=2, h=6144))
+    d = P.tuned(d, bwd=path)
     _say(f"[case] launch by launch, path {path}")
     inp = make_inputs(d.rows, d.h, d.io, seed=4, dh_out=True)
     saved = P.oracle_fwd(od, inp)
