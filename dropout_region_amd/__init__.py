@@ -110,6 +110,8 @@ def lib():
         L.sp_region_fwd_rs.restype = ctypes.c_int
         L.sp_region_bwd.argtypes = [D] + [P] * 12 + [P, ctypes.c_size_t, P]
         L.sp_region_bwd.restype = ctypes.c_int
+        L.sp_region_bwd_noalloc.argtypes = [D] + [P] * 12 + [P]
+        L.sp_region_bwd_noalloc.restype = ctypes.c_int
         L.sp_region_bwd_exit.argtypes = [D, P, P, P, P, P, ctypes.c_size_t, P]
         L.sp_region_bwd_exit.restype = ctypes.c_int
         L.sp_region_bwd_num_launches.argtypes = [D]
@@ -260,6 +262,26 @@ def sp_region_bwd(d, dy, dh_out, h, mask, mean, rstd, gamma, dx_out, dres_out, d
     st = lib().sp_region_bwd(ctypes.byref(d.c()), *args, _stream(stream))
     if st != SPR_OK:
         raise SprError("sp_region_bwd", st)
+
+
+def sp_region_bwd_noalloc(d, dy, dh_out, h, mask, mean, rstd, gamma, dx_out, dres_out,
+                          dgamma_out, dbeta_out, dbias_out, stream=None):
+    """sp_region_bwd with the library's own fixed scratch instead of a
+    workspace (for callers that cannot allocate)."""
+    import torch
+    N, H, io, dev = d.rows, d.h, _io_dtype(d), _dev(dy)
+    f32, u8 = torch.float32, torch.uint8
+    args = [_arg(dy, "dy", N * H, io, dev), _arg(dh_out, "dh_out", N * H, io, dev, True),
+            _arg(h, "h", N * H, io, dev), _arg(mask, "mask", N * H, u8, dev, True),
+            _arg(mean, "mean", N, f32, dev, True), _arg(rstd, "rstd", N, f32, dev),
+            _arg(gamma, "gamma", H, f32, dev), _arg(dx_out, "dx_out", N * H, io, dev, True),
+            _arg(dres_out, "dres_out", N * H, io, dev),
+            _arg(dgamma_out, "dgamma_out", H, f32, dev),
+            _arg(dbeta_out, "dbeta_out", H, f32, dev, True),
+            _arg(dbias_out, "dbias_out", H, f32, dev, True)]
+    st = lib().sp_region_bwd_noalloc(ctypes.byref(d.c()), *args, _stream(stream))
+    if st != SPR_OK:
+        raise SprError("sp_region_bwd_noalloc", st)
 
 
 def sp_region_bwd_exit(d, dh_out, mask, dx_out, dbias_out, workspace, stream=None):

@@ -146,7 +146,8 @@ struct BwdPlan {
     int exit_tile_rows;    // norm-free exit: rows per tile
     int64_t exit_row_blocks;  // norm-free exit: partial rows
     size_t rowpart_bytes;  // split: offset of the column partials in the workspace
-    size_t workspace;      // bytes any of the three needs (the largest)
+    size_t bwd_workspace;  // bytes the chosen backward path needs
+    size_t workspace;      // bytes the backward or the norm-free exit needs (the larger)
 };
 
 bool make_bwd_plan(const spr_desc& d, BwdPlan* plan);

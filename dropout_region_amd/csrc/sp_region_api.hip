@@ -178,15 +178,14 @@ bool make_bwd_plan(const spr_desc& d, BwdPlan* plan) {
     p.exit_row_blocks = (rows + tr_exit - 1) / tr_exit;
     p.rowpart_bytes = round256((uint64_t)rows * 2u * sizeof(float));
 
+    p.path = fused_ok ? kBwdFused : kBwdSplit;
+    if (d.bwd_path == SPR_BWD_SPLIT) p.path = kBwdSplit;
+
     const uint64_t fused_ws = (uint64_t)p.teams * 3u * (uint64_t)d.h * sizeof(float);
     const uint64_t split_ws = p.rowpart_bytes + (uint64_t)p.row_blocks * 3u * (uint64_t)d.h * sizeof(float);
     const uint64_t exit_ws = (uint64_t)p.exit_row_blocks * (uint64_t)d.h * sizeof(float);
-    uint64_t ws = fused_ws > split_ws ? fused_ws : split_ws;
-    if (exit_ws > ws) ws = exit_ws;
-    p.workspace = round256(ws);
-
-    p.path = fused_ok ? kBwdFused : kBwdSplit;
-    if (d.bwd_path == SPR_BWD_SPLIT) p.path = kBwdSplit;
+    p.bwd_workspace = round256(p.path == kBwdFused ? fused_ws : split_ws);
+    p.workspace = p.bwd_workspace > round256(exit_ws) ? p.bwd_workspace : round256(exit_ws);
     *plan = p;
     return true;
 }
@@ -350,12 +349,24 @@ spr_status sp_region_fwd_rs(const spr_desc* d, const void* x_parts, int32_t npar
 
 namespace {
 
-// Every check of the backward, then the kernel arguments and plan.
+// The backward's workspace in the kernel arguments: the split path's per-row
+// sums first, then the column partials.
+void set_workspace(const BwdPlan& plan, void* workspace, BwdArgs* a) {
+    const bool split = plan.path == kBwdSplit;
+    a->rowpart = static_cast<float*>(workspace);
+    a->partials = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                           (split ? plan.rowpart_bytes : 0));
+}
+
+// Every check of the backward, then the kernel arguments and plan.  With
+// fixed_scratch the workspace is the library's own array (set afterwards):
+// only its size is checked.
 spr_status prepare_bwd(const spr_desc* d, const void* dy, const void* dh_out, const void* h,
                        const uint8_t* mask, const float* mean, const float* rstd,
                        const float* gamma, void* dx_out, void* dres_out, float* dgamma_out,
                        float* dbeta_out, float* dbias_out, void* workspace,
-                       size_t workspace_bytes_given, BwdPlan* plan_out, BwdArgs* args_out) {
+                       size_t workspace_bytes_given, BwdPlan* plan_out, BwdArgs* args_out,
+                       bool fixed_scratch = false) {
     RowPlan rp;
     spr_status st = check_desc(d, &rp, kPlanBackward);
     if (st != SPR_OK) return st;
@@ -372,9 +383,13 @@ spr_status prepare_bwd(const spr_desc* d, const void* dy, const void* dh_out, co
     if (!aligned(mask, 8) || !aligned(mean, 4) || !aligned(rstd, 4) || !aligned(dgamma_out, 4) ||
         !aligned(dbeta_out, 4) || !aligned(dbias_out, 4))
         return SPR_ERR_INVALID_ARG;
-    const size_t need = plan.workspace;
-    if (!workspace || workspace_bytes_given < need || !aligned(workspace, 16))
+    const size_t need = plan.bwd_workspace;
+    if (fixed_scratch) {
+        if (need > workspace_bytes_given) return SPR_ERR_WORKSPACE;
+        workspace = nullptr;
+    } else if (!workspace || workspace_bytes_given < need || !aligned(workspace, 16)) {
         return SPR_ERR_WORKSPACE;
+    }
 
     const int64_t rows = d->s_local * d->b;
     const uint64_t E = (uint64_t)rows * (uint64_t)d->h;
@@ -392,9 +407,7 @@ spr_status prepare_bwd(const spr_desc* d, const void* dy, const void* dh_out, co
     a.dy = dy; a.dh_out = dh_out; a.h = h; a.mask = mask; a.mean = mean; a.rstd = rstd;
     a.gamma = gamma; a.dx_out = dx_out; a.dres_out = dres_out;
     const bool split = plan.path == kBwdSplit;
-    a.rowpart = static_cast<float*>(workspace);
-    a.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                          (split ? plan.rowpart_bytes : 0));
+    set_workspace(plan, workspace, &a);
     a.dgamma_out = dgamma_out; a.dbeta_out = dbeta_out; a.dbias_out = dbias_out;
     a.rows = rows;
     a.hidden = d->h;
@@ -425,6 +438,60 @@ spr_status sp_region_bwd(const spr_desc* d, const void* dy, const void* dh_out, 
                                       dgamma_out, dbeta_out, dbias_out, workspace,
                                       workspace_bytes_given, &plan, &a);
     if (st != SPR_OK) return st;
+    return launch_bwd(*d, plan, a, stream, 0, bwd_num_launches(plan)) == hipSuccess ? SPR_OK
+                                                                                    : SPR_ERR_HIP;
+}
+
+}  // extern "C"
+
+namespace {
+
+// The allocation-free backward's scratch: one fixed array per GPU, in this
+// library's device memory.  Host code never passes `scratch` itself to a
+// kernel (on the host the name is only a stand-in for the symbol); it
+// passes the device address hipGetSymbolAddress gives, looked up once per
+// device and kept.
+static __device__ __align__(256) unsigned char scratch[SPR_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void*> scratch_ptr[kMaxScratchDevices];
+
+// The current device's address of `scratch`, or NULL if it cannot be had.
+void* scratch_address() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    void* p = scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+spr_status sp_region_bwd_noalloc(const spr_desc* d, const void* dy, const void* dh_out,
+                                 const void* h, const uint8_t* mask, const float* mean,
+                                 const float* rstd, const float* gamma, void* dx_out,
+                                 void* dres_out, float* dgamma_out, float* dbeta_out,
+                                 float* dbias_out, hipStream_t stream) {
+    BwdPlan plan;
+    BwdArgs a;
+    const spr_status st = prepare_bwd(d, dy, dh_out, h, mask, mean, rstd, gamma, dx_out, dres_out,
+                                      dgamma_out, dbeta_out, dbias_out, nullptr,
+                                      SPR_NOALLOC_SCRATCH_BYTES, &plan, &a, true);
+    if (st != SPR_OK) return st;
+    void* ws = scratch_address();
+    if (!ws) return SPR_ERR_HIP;
+    set_workspace(plan, ws, &a);
     return launch_bwd(*d, plan, a, stream, 0, bwd_num_launches(plan)) == hipSuccess ? SPR_OK
                                                                                     : SPR_ERR_HIP;
 }

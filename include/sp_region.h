@@ -191,11 +191,12 @@ spr_status sp_region_fwd_rs(const spr_desc* desc, const void* x_parts, int32_t n
                             float* mean_out, float* rstd_out,
                             hipStream_t stream);
 
-/* Bytes of device workspace sp_region_bwd needs for this desc on the
- * current device: fp32 column partials of dgamma/dbeta/dbias (one row of
- * 3*h per row team, as many teams as the device has compute units, or per
- * row tile of the split path) and the split path's per-row sums.  0 on an
- * invalid desc. */
+/* Bytes of device workspace sp_region_bwd (and sp_region_bwd_exit) needs
+ * for this desc on the current device: fp32 column partials of dgamma/
+ * dbeta/dbias (one row of 3*h per row team, as many teams as the device has
+ * compute units, or per row tile of the split path) and the split path's
+ * per-row sums; or the exit's dbias partials (one row of h per 16-row
+ * tile), whichever is larger.  0 on an invalid desc. */
 size_t sp_region_bwd_workspace_bytes(const spr_desc* desc);
 
 /* Backward of the region on one shard, from the forward's saved tensors.
@@ -229,6 +230,33 @@ spr_status sp_region_bwd(const spr_desc* desc,
                          float* dgamma_out, float* dbeta_out, float* dbias_out,
                          void* workspace, size_t workspace_bytes,
                          hipStream_t stream);
+
+/* sp_region_bwd for callers that cannot allocate device memory: code being
+ * captured into a HIP graph, tight serving loops, harnesses that forbid
+ * hipMalloc.  The same arguments, checks, kernels and results (bit for bit)
+ * as sp_region_bwd, without the workspace: its scratch is a fixed array of
+ * SPR_NOALLOC_SCRATCH_BYTES in the library's device memory, one per GPU,
+ * held from the first call on that GPU until the process ends.  The call
+ * allocates nothing and frees nothing.
+ *  - A desc whose backward needs more scratch than the array is
+ *    SPR_ERR_WORKSPACE (checked before anything runs).  64 MiB covers every
+ *    shard the fused path runs (h <= 12288 bf16: at most 256 partial rows of
+ *    3*h fp32) and split-path shards of N rows with N * (8 + 3*h/8) bytes
+ *    <= 64 MiB at the default 32-row tiles: [1024, 4, 25600] fits, the
+ *    [2048, 4, 25600] shard (78.7 MB) does not.
+ *  - Every call on one GPU uses that GPU's array: calls that may overlap on
+ *    one GPU (two streams, or two host threads) race and give undefined
+ *    results; serialise them, or use sp_region_bwd with one workspace each.
+ *  - The array's contents on entry do not matter (the kernels write every
+ *    byte they read first) and are left undefined. */
+#define SPR_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+spr_status sp_region_bwd_noalloc(const spr_desc* desc,
+                                 const void* dy, const void* dh_out, const void* h,
+                                 const uint8_t* mask, const float* mean, const float* rstd,
+                                 const float* gamma,
+                                 void* dx_out, void* dres_out,
+                                 float* dgamma_out, float* dbeta_out, float* dbias_out,
+                                 hipStream_t stream);
 
 /* Backward of the norm-free exit (a forward with gamma == NULL):
  * dh = dh_out, so

@@ -31,7 +31,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["sp_region_fwd", "sp_region_fwd_rs", "sp_region_bwd",
-                            "sp_region_bwd_exit",
+                            "sp_region_bwd_exit", "sp_region_bwd_noalloc",
                             "sp_region_bwd_workspace_bytes",
                             "sp_region_bwd_num_launches", "sp_region_bwd_launch",
                             "sp_region_activation_bytes", "sp_region_status_string",
@@ -292,3 +292,21 @@ def test_activation_bytes_count_the_buffers_a_forward_keeps(L):
         kept = sum(0 if free[k] is None else free[k].numel() * free[k].element_size()
                    for k in ("h", "mask", "mean", "rstd"))
         assert saved - kept == (w.rows * w.h if w.p > 0 else 0), name
+
+
+def test_noalloc_backward_checks(L):
+    """The allocation-free backward checks its arguments like sp_region_bwd,
+    and a shard whose scratch need exceeds the fixed array is
+    SPR_ERR_WORKSPACE -- all on the host, before anything is launched."""
+    G = 1 << 32                                  # fake buffers 4 GiB apart
+
+    def call(d, dy=A):
+        ptrs = [dy, 0, A + 2 * G, A + 3 * G, A + 4 * G, A + 5 * G, A + 6 * G, A + 7 * G,
+                A + 8 * G, A + 9 * G, A + 10 * G, A + 11 * G]
+        return L.sp_region_bwd_noalloc(ctypes.byref(d), *[ctypes.c_void_p(p) for p in ptrs],
+                                       None)
+    assert call(_good_desc(p=2.0)) == spr.SPR_ERR_INVALID_ARG
+    assert call(_good_desc(), dy=0) == spr.SPR_ERR_INVALID_ARG
+    big = _good_desc(s_local=2048, b=4, h=25600)
+    assert L.sp_region_bwd_workspace_bytes(ctypes.byref(big)) > 64 << 20
+    assert call(big) == spr.SPR_ERR_WORKSPACE
