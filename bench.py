@@ -97,10 +97,32 @@ def algorithmic_bytes(w, with_bias=True, with_dh_out=False, mask_stored=True, x_
     return fwd, bwd_rows, n_grad * H * 4
 
 
-def cpu_baseline(w, min_seconds=10.0, max_seconds=30.0):
-    """The CPU oracle (single-threaded C, as it stands) on the same shard:
-    forward + backward over all N rows, repeated until at least min_seconds
-    have passed.  Returns tokens/s and the sample description."""
+def _host_cpu():
+    """(CPU model, logical CPUs the process may use, all logical CPUs)."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    usable = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return model, usable, os.cpu_count()
+
+
+def cpu_baseline(w, seconds=6.0, max_threads=16):
+    """The CPU oracle as it stands (plain C, one row at a time) on the same
+    shard, forward + backward over all N rows, timed twice:
+      - one thread, whole shard, repeated until `seconds` have passed;
+      - every usable host core (at most max_threads: one GPU's share of the
+        host), the rows cut into one contiguous range per thread, each thread
+        running the oracle's forward then backward on its range (the oracle
+        takes row ranges; ctypes releases the GIL during each call); the
+        threads' parameter-gradient partials are added in thread order.
+    Returns the all-core figure (tokens/s) with the one-thread one beside it."""
+    import threading
+    import numpy as np
     import oracle
     from oracle import build as obuild
     from sp_inputs import make_inputs
@@ -110,16 +132,53 @@ def cpu_baseline(w, min_seconds=10.0, max_seconds=30.0):
                      norm=w.norm, p=w.p, eps=w.eps, seed=w.seed, offset=0)
     inp = make_inputs(w.rows, w.h, w.io, seed=w.seed)
     beta = inp["beta"] if w.norm == 0 else None
-    reps, t_total = 0, 0.0
-    while t_total < min_seconds and t_total < max_seconds:
-        t0 = time.perf_counter()
-        o = oracle.fwd(od, inp["x"], inp["bias"], inp["residual"], inp["gamma"], beta)
-        oracle.bwd(od, inp["dy"], None, o["h"], o["mask"], o["mean"], o["rstd"], inp["gamma"])
-        t_total += time.perf_counter() - t0
-        reps += 1
-    return {"value": w.rows * reps / t_total, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"whole shard [{w.s_local}, {w.b}, {w.h}] fwd+bwd x{reps} "
-                      f"({t_total:.1f} s, 1 thread)"}
+    H = w.h
+
+    def run_rows(r0, r1, out, slot):
+        sl = slice(r0 * H, r1 * H)
+        o = oracle.fwd(od, inp["x"][sl], inp["bias"], inp["residual"][sl], inp["gamma"], beta,
+                       rows=(r0, r1))
+        out[slot] = oracle.bwd(od, inp["dy"][sl], None, o["h"], o["mask"], o["mean"], o["rstd"],
+                               inp["gamma"], rows=(r0, r1))
+
+    def timed(fn):
+        reps, total = 0, 0.0
+        while total < seconds:
+            t0 = time.perf_counter()
+            fn()
+            total += time.perf_counter() - t0
+            reps += 1
+        return reps, total
+
+    one = [None]
+    reps1, t1 = timed(lambda: run_rows(0, w.rows, one, 0))
+    model, usable, nproc = _host_cpu()
+    nt = max(1, min(usable, max_threads, w.rows))
+    cuts = [w.rows * i // nt for i in range(nt + 1)]
+
+    def all_cores():
+        parts = [None] * nt
+        th = [threading.Thread(target=run_rows, args=(cuts[i], cuts[i + 1], parts, i))
+              for i in range(nt)]
+        for t in th:
+            t.start()
+        for t in th:
+            t.join()
+        grads = {k: np.zeros(H, np.float64) for k in ("dgamma", "dbeta", "dbias")}
+        for p in parts:                       # thread order
+            for k in grads:
+                if p[k] is not None:
+                    grads[k] += p[k]
+        return grads
+
+    repsn, tn = timed(all_cores)
+    return {"value": round(w.rows * repsn / tn, 1), "unit": "tokens/s", "cores": nt,
+            "kind": "oracle",
+            "sample": f"whole shard [{w.s_local}, {w.b}, {w.h}] fwd+bwd x{repsn} on {nt} threads "
+                      f"(rows cut into {nt} ranges; {tn:.1f} s); one thread: x{reps1} "
+                      f"({t1:.1f} s)",
+            "one_core": {"value": round(w.rows * reps1 / t1, 1), "cores": 1},
+            "cpu_model": model, "nproc": nproc, "usable_cpus": usable}
 
 
 def copy_bandwidth(torch, nbytes=COPY_BYTES, iters=20):
@@ -381,6 +440,12 @@ def main():
     ap.add_argument("--no-mask", action="store_true",
                     help="mask-free region: the forward stores no mask, the backward "
                          "regenerates the dropout decisions")
+    ap.add_argument("--fwd-kernel", choices=("auto", "rows", "stream"), default="auto",
+                    help="the forward kernel (a launch choice of the descriptor)")
+    ap.add_argument("--bwd-path", choices=("auto", "fused", "split"), default="auto",
+                    help="the backward path (a launch choice of the descriptor)")
+    ap.add_argument("--tile-rows", type=int, default=0,
+                    help="rows per tile of the split backward and the exit (0: the library's)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--stats-summary", metavar="TRACE_DIR")
     ap.add_argument("--counters-summary", metavar="PMC_DIR")
@@ -414,7 +479,10 @@ def main():
     dev = torch.device("cuda:0")
     V = args.variant
     d = spr.Desc(s_local=w.s_local, b=w.b, h=w.h, shard_index=0, t=w.t, io=w.io, norm=w.norm,
-                 p=0.0 if V == "entry" else w.p, eps=w.eps, seed=w.seed, offset=0)
+                 p=0.0 if V == "entry" else w.p, eps=w.eps, seed=w.seed, offset=0,
+                 fwd_kernel={"auto": 0, "rows": 1, "stream": 2}[args.fwd_kernel],
+                 bwd_path={"auto": 0, "fused": 1, "split": 2}[args.bwd_path],
+                 bwd_tile_rows=args.tile_rows)
     if V != "full" and (args.rs_parts or args.no_mask):
         sys.exit("bench.py: --variant takes neither --rs-parts nor --no-mask")
     spr.lib()
@@ -541,6 +609,36 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = ev0.elapsed_time(ev1) / args.steps
+
+    # ---- the same steps with an event after each: the distribution of the
+    # step time (median, p10, p90)
+    def step_times(order):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        torch.cuda.synchronize()
+        evs[0].record(stream)
+        for i in range(args.steps):
+            order(i)
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+        return np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]) * 1e3
+
+    def same_set(i):
+        s = sets[i % nsets]
+        fwd(s)
+        bwd(s)
+
+    # The backward of step i reads the set the forward of step i - nsets/2
+    # wrote: h and the mask were written half the rotation (>= 512 MB of
+    # traffic) earlier, so they come from HBM, not from the Infinity Cache a
+    # same-set step may find them in.
+    lag = nsets // 2
+
+    def lagged(i):
+        fwd(sets[i % nsets])
+        bwd(sets[(i - lag) % nsets])
+
+    per_step_us = step_times(same_set)
+    lagged_us = step_times(lagged)
 
     # ---- timed region 2: each kernel alone.  A chunk of back-to-back
     # launches of one kernel is captured in a HIP graph and replayed between
@@ -703,11 +801,19 @@ def main():
                    if w.p > 0 else "none (p = 0)"},
         "hbm_gbps": round(gbps, 1), "hbm_frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4),
         "copy_gbps": round(copy_gbps, 1), "frac_of_copy": round(gbps / copy_gbps, 4),
+        "launch_choices": {"fwd_kernel": args.fwd_kernel, "bwd_path": args.bwd_path,
+                           "bwd_tile_rows": args.tile_rows or "auto"},
         "kernels_us": {n: round(float(u), 2) for n, u in zip(names, kernel_us)},
         "kernels_us_p10_p90": {n: [round(float(np.percentile(per_kernel_ms[:, k], q)) * 1e3, 2)
                                    for q in (10, 90)] for k, n in enumerate(names)},
         "kernel_timing": f"HIP events around replays of a HIP graph of {chunk} launches of one kernel",
         "algorithmic_bytes": {"fwd": fwd_b, "bwd": bwd_rows_b + bwd_grad_b},
+        "step_us_median": round(float(np.median(per_step_us)), 2),
+        "step_us_p10_p90": [round(float(np.percentile(per_step_us, q)), 2) for q in (10, 90)],
+        "step_us_lagged_bwd_median": round(float(np.median(lagged_us)), 2),
+        "step_timing": "ms_per_step and value: HIP events around all K steps; step_us_*: an event "
+                       "after every step (a second pass of K steps); lagged_bwd: the backward "
+                       f"of step i reads the set step i - {lag} wrote",
         "wall_s_timed_region": round(wall, 4),
         "host_enqueue_us_per_step": round(t_enqueued / args.steps * 1e6, 2),
         "graph_step_us": round(graph_step_us, 2),

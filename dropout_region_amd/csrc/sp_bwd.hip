@@ -32,7 +32,16 @@ struct RowIn {
     float mu, rs;
 };
 
-template <typename IO, int NORM, int DROP, int VPT, bool WAVE_ROWS, int LB>
+// Keep decision of element j of a vector from its mask words (one byte per
+// element; any nonzero byte keeps).
+template <int MW>
+__device__ __forceinline__ bool mask_keeps(const uint32_t (&w)[MW], int j) {
+    return ((w[j >> 2] >> (8 * (j & 3))) & 0xffu) != 0u;
+}
+
+// EXACT: every vector slot of the team holds a vector of the row (no idle
+// slot to mask out of the sums).
+template <typename IO, int NORM, int DROP, int VPT, bool WAVE_ROWS, int LB, bool EXACT>
 __global__ void __launch_bounds__(LB) sp_region_bwd_rows_kernel(BwdArgs a) {
     // Rows in flight per thread (each costs the row's registers again).
     constexpr int DEPTH = bwd_depth(VPT, LB, WAVE_ROWS, NORM == SPR_LAYERNORM);
@@ -62,7 +71,7 @@ __global__ void __launch_bounds__(LB) sp_region_bwd_rows_kernel(BwdArgs a) {
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
         const int vec = k * tpr + tid;
-        ok[k] = vec < a.nvec;
+        ok[k] = EXACT || vec < a.nvec;
         vc[k] = ok[k] ? vec : a.nvec - 1;
     }
 
@@ -94,7 +103,12 @@ __global__ void __launch_bounds__(LB) sp_region_bwd_rows_kernel(BwdArgs a) {
     };
 
     // One row: the two row sums (one team reduction through `slot`), then
-    // dx/dresidual and the column partials.
+    // dx/dresidual and the column partials.  With d = h - mean (RMSNorm:
+    // d = h), xhat = d * rstd and g = dy * gamma,
+    //   dh = rstd * (g - mean_c(g) - xhat * mean_c(g * xhat))
+    //      = rstd * g - c1 - c2 * d,   c1 = rstd * mean_c(g),
+    //                                  c2 = rstd^3 * mean_c(g * d)
+    // (RMSNorm: c1 = 0), two FMAs per element after the row constants.
     auto process = [&](int64_t row, const RowIn<VPT, MW>& cur, float* slot) {
         // Regenerated dropout: the row's keep bits.
         uint32_t kbits[VPT];
@@ -106,51 +120,48 @@ __global__ void __launch_bounds__(LB) sp_region_bwd_rows_kernel(BwdArgs a) {
                                         a.off_lo, a.off_hi, a.key_lo, a.key_hi, a.thr);
         }
 
-        V hv[VPT], dyv[VPT];
+        const float rs = cur.rs;
+        float d[VPT][E], dyf[VPT][E];
         float s1 = 0.0f, s2 = 0.0f;
 #pragma unroll
         for (int k = 0; k < VPT; ++k) {
-            hv[k].set(cur.h[k]);
-            dyv[k].set(cur.dy[k]);
+            V hv, dv;
+            hv.set(cur.h[k]);
+            dv.set(cur.dy[k]);
 #pragma unroll
             for (int j = 0; j < E; ++j) {
-                const float xh = (hv[k].v[j] - cur.mu) * cur.rs;
-                const float g = dyv[k].v[j] * gam[k][j];
+                d[k][j] = (NORM == SPR_LAYERNORM) ? hv.v[j] - cur.mu : hv.v[j];
+                dyf[k][j] = dv.v[j];
+                const float g = dv.v[j] * gam[k][j];
                 if (ok[k]) {
                     s1 += g;
-                    s2 += g * xh;
+                    s2 = fmaf(g, d[k][j], s2);
                 }
             }
         }
         block_sum2(s1, s2, slot, nwaves);
-        const float mg = s1 * a.inv_h, mgx = s2 * a.inv_h;
+        const float c1 = (NORM == SPR_LAYERNORM) ? rs * (s1 * a.inv_h) : 0.0f;
+        const float c2 = rs * (rs * (rs * (s2 * a.inv_h)));   // 0 when s2 is, whatever rs
 
         const int64_t rbase = row * a.hidden;
 #pragma unroll
         for (int k = 0; k < VPT; ++k) {
             V dho, dres, dx;
             if (a.dh_out) dho.set(cur.dho[k]);
-            uint32_t kb = 0xffu;
-            if (DROP == kDropMask) {
-                kb = MaskBytes<4>::from_word(cur.mask[k][0]);
-                if (MW == 2) kb |= MaskBytes<4>::from_word(cur.mask[k][MW - 1]) << 4;
-            } else if (DROP == kDropRegen) {
-                kb = kbits[k];
-            }
 #pragma unroll
             for (int j = 0; j < E; ++j) {
-                const float xh = (hv[k].v[j] - cur.mu) * cur.rs;
-                const float g = dyv[k].v[j] * gam[k][j];
-                float dh = (NORM == SPR_LAYERNORM) ? cur.rs * (g - mg - xh * mgx)
-                                                   : cur.rs * (g - xh * mgx);
+                const float g = dyf[k][j] * gam[k][j];
+                float dh = fmaf(rs, g, fmaf(-c2, d[k][j], -c1));
                 if (a.dh_out) dh += dho.v[j];
-                const float dxu =
-                    DROP != kDropNone ? (((kb >> j) & 1u) ? dh * a.scale : 0.0f) : dh;
+                bool keep = true;
+                if (DROP == kDropMask) keep = mask_keeps<MW>(cur.mask[k], j);
+                else if (DROP == kDropRegen) keep = ((kbits[k] >> j) & 1u) != 0u;
+                const float dxu = DROP != kDropNone ? (keep ? dh * a.scale : 0.0f) : dh;
                 dres.v[j] = dh;
                 dx.v[j] = dxu;
                 if (ok[k]) {
-                    acc_g[k][j] += dyv[k].v[j] * xh;
-                    acc_b[k][j] += dyv[k].v[j];
+                    acc_g[k][j] = fmaf(dyf[k][j], d[k][j] * rs, acc_g[k][j]);
+                    acc_b[k][j] += dyf[k][j];
                     acc_x[k][j] += dxu;
                 }
             }
@@ -594,12 +605,13 @@ int64_t bwd_teams(const spr_desc& d, const RowPlan& p) {
     return ((want + p.rpw - 1) / p.rpw) * p.rpw;
 }
 
-template <typename IO, int NORM, int DROP, bool WR>
+template <typename IO, int NORM, int DROP, bool WR, bool EXACT>
 static hipError_t bwd_by_vpt(const RowPlan& p, const BwdArgs& a, hipStream_t s) {
     const dim3 g((unsigned)(a.teams / p.rpw)), b((unsigned)p.block);
 #define SPR_BWD_CASE(V, L)                                                                       \
     case V:                                                                                      \
-        hipLaunchKernelGGL((sp_region_bwd_rows_kernel<IO, NORM, DROP, V, WR, L>), g, b, 0, s, a); \
+        hipLaunchKernelGGL((sp_region_bwd_rows_kernel<IO, NORM, DROP, V, WR, L, EXACT>), g, b, 0, \
+                           s, a);                                                                \
         break;
     if constexpr (WR) {
         switch (p.vpt) {
@@ -611,11 +623,11 @@ static hipError_t bwd_by_vpt(const RowPlan& p, const BwdArgs& a, hipStream_t s) 
         switch (p.vpt) {
             case 1:
                 if (p.lb == 768) {
-                    hipLaunchKernelGGL((sp_region_bwd_rows_kernel<IO, NORM, DROP, 1, WR, 768>), g, b,
-                                       0, s, a);
+                    hipLaunchKernelGGL((sp_region_bwd_rows_kernel<IO, NORM, DROP, 1, WR, 768, EXACT>),
+                                       g, b, 0, s, a);
                 } else {
-                    hipLaunchKernelGGL((sp_region_bwd_rows_kernel<IO, NORM, DROP, 1, WR, 1024>), g,
-                                       b, 0, s, a);
+                    hipLaunchKernelGGL((sp_region_bwd_rows_kernel<IO, NORM, DROP, 1, WR, 1024, EXACT>),
+                                       g, b, 0, s, a);
                 }
                 break;
             SPR_BWD_CASE(2, 768) SPR_BWD_CASE(3, 512)
@@ -636,8 +648,12 @@ static hipError_t launch_finalize(const BwdArgs& a, hipStream_t s) {
 
 template <typename IO, int NORM, int DROP>
 static hipError_t bwd_by_mode(const RowPlan& p, const BwdArgs& a, hipStream_t s) {
-    return p.rpw > 1 ? bwd_by_vpt<IO, NORM, DROP, true>(p, a, s)
-                     : bwd_by_vpt<IO, NORM, DROP, false>(p, a, s);
+    const bool exact = p.nvec == p.vpt * p.tpr;
+    if (p.rpw > 1)
+        return exact ? bwd_by_vpt<IO, NORM, DROP, true, true>(p, a, s)
+                     : bwd_by_vpt<IO, NORM, DROP, true, false>(p, a, s);
+    return exact ? bwd_by_vpt<IO, NORM, DROP, false, true>(p, a, s)
+                 : bwd_by_vpt<IO, NORM, DROP, false, false>(p, a, s);
 }
 
 template <typename IO, int NORM, bool WR, bool EXACT>

@@ -237,12 +237,40 @@ template <> struct HVec<float> {
 };
 
 // ------------------------------------------------------------------ reductions
-// Sum over the 64 lanes of a wave; every lane gets the same bits (each
-// butterfly step adds the same two operands on both partners).
+// Lane exchanges inside 16-lane rows by DPP (data-parallel primitives: the
+// VALU reads the other lane's register directly, no LDS round trip).  Each
+// control pairs a lane with one in the same row: quad_perm [1,0,3,2] and
+// [2,3,0,1] swap neighbours at distance 1 and 2; row_half_mirror maps lane i
+// of each 8-lane half to 7-i, row_mirror lane i of the row to 15-i.  Applied
+// in that order to values that are already equal within the groups the
+// earlier steps formed, each mirror pairs a group with its neighbour group,
+// like an exchange at distance 4 and then 8.
+enum : int {
+    kDppXor1 = 0xB1,           // quad_perm [1,0,3,2]
+    kDppXor2 = 0x4E,           // quad_perm [2,3,0,1]
+    kDppHalfMirror = 0x141,    // row_half_mirror
+    kDppMirror = 0x140         // row_mirror
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float lane_value(float v, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// Sum over the 64 lanes of a wave, every lane getting the same bits: a
+// butterfly inside each 16-lane row (each step adds the same two operands
+// on both partners), then the four row sums, read from lanes 0, 16, 32 and
+// 48, added as (r0 + r1) + (r2 + r3).  Needs all 64 lanes active.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
+    v += dpp<kDppXor1>(v);
+    v += dpp<kDppXor2>(v);
+    v += dpp<kDppHalfMirror>(v);
+    v += dpp<kDppMirror>(v);
+    return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
 }
 
 // Sum over the waves of a workgroup that owns one row.  `slot` points to
@@ -276,9 +304,24 @@ __device__ __forceinline__ MeanM2 merge(MeanM2 a, MeanM2 b) {
     return {n, a.mean + d * wb, a.m2 + b.m2 + d * d * a.n * wb};
 }
 
+// One butterfly step of the wave merge: partner by DPP control CTRL, the
+// operand from the lower lane group first (bit `low` of the lane index
+// clear), so both partners evaluate the same expression.
+template <int CTRL>
+__device__ __forceinline__ MeanM2 merge_step(MeanM2 v, int lane, int low) {
+    const MeanM2 o{dpp<CTRL>(v.n), dpp<CTRL>(v.mean), dpp<CTRL>(v.m2)};
+    const bool upper = (lane & low) != 0;
+    return merge(upper ? o : v, upper ? v : o);
+}
+
+__device__ __forceinline__ MeanM2 lane_value(MeanM2 v, int lane) {
+    return {lane_value(v.n, lane), lane_value(v.mean, lane), lane_value(v.m2, lane)};
+}
+
 // Team-wide merge of per-thread (count, mean, M2), the means taken relative
 // to a pivot `piv` that is the same across each wave (a value of the row):
-// wave butterflies, then the waves' results in wave order through `slot`
+// DPP butterflies inside each wave's rows and its rows' results in row
+// order, then the waves' results in wave order through `slot`
 // (4 x 16 floats of LDS), each wave's mean first moved into wave 0's frame
 // ((piv_w - piv_0) + mean_w, both differences of nearby values).  Returns
 // the merge relative to wave 0's pivot, which `piv0` receives.  With the
@@ -287,13 +330,13 @@ __device__ __forceinline__ MeanM2 merge(MeanM2 a, MeanM2 b) {
 __device__ __forceinline__ MeanM2 block_mean_m2(MeanM2 v, float piv, float* slot, int nwaves,
                                                 float& piv0) {
     const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int off = 1; off <= 32; off <<= 1) {
-        const MeanM2 o{__shfl_xor(v.n, off, 64), __shfl_xor(v.mean, off, 64),
-                       __shfl_xor(v.m2, off, 64)};
-        const bool upper = (lane & off) != 0;
-        v = merge(upper ? o : v, upper ? v : o);
-    }
+    v = merge_step<kDppXor1>(v, lane, 1);
+    v = merge_step<kDppXor2>(v, lane, 2);
+    v = merge_step<kDppHalfMirror>(v, lane, 4);
+    v = merge_step<kDppMirror>(v, lane, 8);
+    // the four rows' results, merged in row order
+    v = merge(merge(lane_value(v, 0), lane_value(v, 16)),
+              merge(lane_value(v, 32), lane_value(v, 48)));
     piv0 = piv;
     if (nwaves == 1) return v;
     const int wave = threadIdx.x >> 6;
