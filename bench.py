@@ -40,7 +40,7 @@ COPY_BYTES = 1 << 30             # the plain copy the counters are calibrated on
 # sources are stale.
 REGION_SOURCES = ("sp_device.h", "sp_plan.h", "sp_host_checks.h", "sp_fwd.hip", "sp_bwd.hip",
                   "sp_region_api.hip")
-ATTN_SOURCES = ("sp_device.h", "sp_host_checks.h", "ring_attn.hip")
+ATTN_SOURCES = ("sp_device.h", "sp_plan.h", "sp_host_checks.h", "ring_attn.hip")
 
 
 def kernel_source_hash(workload=None):
@@ -201,6 +201,26 @@ def copy_bandwidth(torch, nbytes=COPY_BYTES, iters=20):
 
 
 # ------------------------------------------------------------------ summaries
+def profile_key(workload, args):
+    """Name of a workload's profile summaries: the workload, then the
+    variant (entry, exit), the mask-free region (nomask), the reduce-scatter
+    prologue (rsK) and any launch choice that is not the library's own."""
+    key = workload
+    if getattr(args, "variant", "full") != "full":
+        key += "_" + args.variant
+    if getattr(args, "no_mask", False):
+        key += "_nomask"
+    if getattr(args, "rs_parts", 0):
+        key += f"_rs{args.rs_parts}"
+    if getattr(args, "fwd_kernel", "auto") != "auto":
+        key += f"_fwd{args.fwd_kernel}"
+    if getattr(args, "bwd_path", "auto") != "auto":
+        key += f"_bwd{args.bwd_path}"
+    if getattr(args, "tile_rows", 0):
+        key += f"_tile{args.tile_rows}"
+    return key
+
+
 def _profile_name(workload, what):
     prefix = "" if workload.startswith("ring_attn") else "sp_region_"
     return os.path.join(PROFILES, f"{prefix}{workload}_{what}")
@@ -236,7 +256,7 @@ def pmc_summary(fetch_dir, write_dir, workload, command):
            "copy_kernel": copy_name, "copy_bytes": COPY_BYTES,
            "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4), "kernels": {}}
     for k in fetch:
-        if "sp_region" not in k:
+        if "sp_region" not in k and "ring_attn" not in k:
             continue
         wv = write.get(k, [0.0])
         out["kernels"][_short(k)] = {
@@ -454,12 +474,13 @@ def main():
 
     from sp_inputs import HEADLINE, WORKLOADS
     wname = args.workload or HEADLINE
+    key = profile_key(wname, args)
     if args.pmc_summary:
-        return pmc_summary(*args.pmc_summary, wname, args.command)
+        return pmc_summary(*args.pmc_summary, key, args.command)
     if args.stats_summary:
-        return stats_summary(args.stats_summary, wname, args.command)
+        return stats_summary(args.stats_summary, key, args.command)
     if args.counters_summary:
-        return counters_summary(args.counters_summary, wname, args.command)
+        return counters_summary(args.counters_summary, key, args.command)
     if args.gpus != 1:
         print(f"bench.py: the benchmark runs on one GPU; --gpus {args.gpus} is not supported "
               "(the region is per-rank; there are no collectives to run)", file=sys.stderr)
@@ -779,7 +800,7 @@ def main():
     gbps = total_alg / (ms_per_step / 1e3) / 1e9
     dom = int(np.argmax(kernel_us))
     achieved = alg[dom] / (kernel_us[dom] / 1e6) / 1e9
-    traffic = load_traffic(w.name)
+    traffic = load_traffic(profile_key(w.name, args))
     dom_traffic = None
     aliases = {"sp_region_fwd": ("sp_region_fwd_kernel", "sp_region_fwd_stream_kernel")}
     for kname in aliases.get(names[dom], (names[dom],)):
