@@ -631,17 +631,22 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = ev0.elapsed_time(ev1) / args.steps
 
-    # ---- the same steps with an event after each: the distribution of the
-    # step time (median, p10, p90)
+    # ---- the same steps with an event after every `per` steps: the
+    # distribution (median, p10, p90) of the step time averaged over each
+    # group of `per` (an event after every step would itself add ~2 us a step)
+    per = 5
+
     def step_times(order):
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        n = max(1, args.steps // per)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
         torch.cuda.synchronize()
         evs[0].record(stream)
-        for i in range(args.steps):
-            order(i)
-            evs[i + 1].record(stream)
+        for c in range(n):
+            for i in range(c * per, (c + 1) * per):
+                order(i)
+            evs[c + 1].record(stream)
         torch.cuda.synchronize()
-        return np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]) * 1e3
+        return np.array([evs[c].elapsed_time(evs[c + 1]) / per for c in range(n)]) * 1e3
 
     def same_set(i):
         s = sets[i % nsets]
@@ -720,6 +725,37 @@ def main():
     torch.cuda.synchronize()
     graph_step_us = g0.elapsed_time(g1) / (n_chunks * chunk) * 1e3
     del g
+
+    # ---- whole steps as above, with the backward's last launch (the
+    # fixed-order column finalize of dgamma/dbeta/dbias) on a second stream
+    # so that it overlaps the next step's forward, as a training step may
+    # schedule it (nothing downstream of the region's backward reads the
+    # parameter gradients before the optimizer).  Forked from and joined to
+    # the capture stream inside the graph; every launch is replayed.
+    graph_overlap_us = None
+    if V == "full" and n_bwd >= 2 and chunk <= nsets:
+        side = torch.cuda.Stream()               # default priority
+        g = torch.cuda.CUDAGraph()
+        cap_stream.wait_stream(stream)
+        with torch.cuda.graph(g, stream=cap_stream):
+            for i in range(chunk):               # distinct sets: no reuse inside the graph
+                s = sets[i % nsets]
+                fwd(s, stream=None)
+                for k in range(n_bwd - 1):
+                    spr.sp_region_bwd_launch(d, k, *bwd_args(s), None)
+                side.wait_stream(cap_stream)
+                spr.sp_region_bwd_launch(d, n_bwd - 1, *bwd_args(s), side)
+            cap_stream.wait_stream(side)
+        stream.wait_stream(cap_stream)
+        g.replay()
+        torch.cuda.synchronize()
+        g0.record(stream)
+        for _ in range(n_chunks):
+            g.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        graph_overlap_us = g0.elapsed_time(g1) / (n_chunks * chunk) * 1e3
+        del g
 
     # ---- the reduce-scatter prologue against its unfused form (torch's sum of
     # the slabs, fp32 accumulation, into x; then sp_region_fwd), eager
@@ -832,9 +868,15 @@ def main():
         "step_us_median": round(float(np.median(per_step_us)), 2),
         "step_us_p10_p90": [round(float(np.percentile(per_step_us, q)), 2) for q in (10, 90)],
         "step_us_lagged_bwd_median": round(float(np.median(lagged_us)), 2),
+        "graph_step_us_finalize_on_second_stream": (round(graph_overlap_us, 2)
+                                                    if graph_overlap_us is not None else None),
         "step_timing": "ms_per_step and value: HIP events around all K steps; step_us_*: an event "
-                       "after every step (a second pass of K steps); lagged_bwd: the backward "
-                       f"of step i reads the set step i - {lag} wrote",
+                       f"after every {per} steps (a second pass of K steps), the distribution of "
+                       "those groups' mean step; lagged_bwd: the backward "
+                       f"of step i reads the set step i - {lag} wrote; graph_step_us: whole steps "
+                       "replayed from a HIP graph; ..._finalize_on_second_stream: the same with "
+                       "the backward's column finalize on a second stream, overlapping the next "
+                       "forward",
         "wall_s_timed_region": round(wall, 4),
         "host_enqueue_us_per_step": round(t_enqueued / args.steps * 1e6, 2),
         "graph_step_us": round(graph_step_us, 2),
