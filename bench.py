@@ -284,10 +284,12 @@ def stats_summary(trace_dir, workload, command):
     print(path)
 
 
-def counters_summary(pmc_dir, workload, command):
-    """Markdown table of the counters of a rocprofv3 --pmc run, averaged per
-    dispatch for each kernel of the workload."""
-    rows = list(csv.DictReader(open(glob.glob(os.path.join(pmc_dir, "*counter_collection.csv"))[0])))
+def counters_summary(pmc_dirs, workload, command):
+    """Markdown table of the counters of one or more rocprofv3 --pmc runs (one
+    per pass), averaged per dispatch for each kernel of the workload."""
+    rows = []
+    for pmc_dir in pmc_dirs:
+        rows += list(csv.DictReader(open(glob.glob(os.path.join(pmc_dir, "*counter_collection.csv"))[0])))
     by = {}
     for r in rows:
         k = _short(r["Kernel_Name"])
@@ -468,7 +470,7 @@ def main():
                     help="rows per tile of the split backward and the exit (0: the library's)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--stats-summary", metavar="TRACE_DIR")
-    ap.add_argument("--counters-summary", metavar="PMC_DIR")
+    ap.add_argument("--counters-summary", nargs="+", metavar="PMC_DIR")
     ap.add_argument("--command", default="", help="command recorded in a summary")
     args = ap.parse_args()
 

@@ -96,7 +96,10 @@ __global__ void __launch_bounds__(64 * W, W == 4 ? 2 : 1) ring_attn_step_kernel(
     constexpr int KS = D / 16;          // k-steps of S^T = K Q^T
     constexpr int DB = D / 32;          // 32-row blocks of O^T
     constexpr int KP = D + 8;           // K tile pitch (elements)
-    constexpr int VP = kKT + 8;         // transposed V tile pitch
+    // Transposed V tile pitch: 80 elements (160 bytes).  Measured on MI355X
+    // (SQ_LDS_BANK_CONFLICT), pitches of 72 or 88 stall the LDS five times as
+    // many cycles on bank conflicts as 80 or 112 (64-key tiles, d = 128).
+    constexpr int VP = kKT + 16;
     constexpr int CH = kKT * D / 8;     // 16-byte chunks per K (or V) tile
     constexpr int CPT = CH / NT;        // chunks per thread
     static_assert(CH % NT == 0, "tile chunks must split evenly over the workgroup");
@@ -389,7 +392,7 @@ static hipError_t launch_step(const AttnArgs& a, int steps, hipStream_t s) {
     // One grid dimension: query tiles x (batch, head) x groups of steps, at
     // most 2^31 - 1 (the descriptor checks bound it).
     const dim3 g((unsigned)((a.s_local + 32 * W - 1) / (32 * W) * a.b * a.heads * steps));
-    constexpr size_t lds = 2 * ((size_t)kKT * (D + 8) + (size_t)D * (kKT + 8)) * sizeof(__bf16);
+    constexpr size_t lds = 2 * ((size_t)kKT * (D + 8) + (size_t)D * (kKT + 16)) * sizeof(__bf16);
     // The dynamic LDS allowance is set once per device (bit d of `done`).
     static std::atomic<uint64_t> done{0};
     int dev = 0;
