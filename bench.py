@@ -16,6 +16,8 @@ current kernel sources), and the CPU oracle timed on the host.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
     python bench.py --pmc-summary FETCH_DIR WRITE_DIR    (writes profiles/..._hbm_traffic.json)
     python bench.py --stats-summary TRACE_DIR            (writes profiles/..._kernel_stats.md)
+    python bench.py --counters-summary PMC_DIR [...]     (writes profiles/..._counters.md, one
+                                                          directory per rocprofv3 --pmc pass)
 """
 import argparse
 import csv
