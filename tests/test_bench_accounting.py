@@ -64,3 +64,30 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def _pmc_csv(path, rows):
+    import csv
+    import os
+    os.makedirs(path, exist_ok=True)
+    with open(os.path.join(path, "run_counter_collection.csv"), "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for r in rows:
+            w.writerow(dict(zip(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"], r)))
+
+
+def test_counters_summary_merges_passes(tmp_path, monkeypatch):
+    """Two --pmc passes (different counters) go into one table, each counter
+    averaged over its dispatches; kernels outside the library are left out."""
+    step = "spr::ring_attn_step_kernel<128, true>(spr::AttnArgs)"
+    _pmc_csv(str(tmp_path / "p1"), [(1, step, "SQ_WAVES", 10), (2, step, "SQ_WAVES", 30),
+                                    (3, "elementwise_kernel", "SQ_WAVES", 99)])
+    _pmc_csv(str(tmp_path / "p2"), [(1, step, "SQ_LDS_BANK_CONFLICT", 4), (2, step, "SQ_LDS_BANK_CONFLICT", 8)])
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    bench.counters_summary([str(tmp_path / "p1"), str(tmp_path / "p2")], "ring_attn_s2k_t8_d128", "cmd")
+    text = (tmp_path / "ring_attn_s2k_t8_d128_counters.md").read_text()
+    assert "## ring_attn_step_kernel" in text
+    assert "| SQ_WAVES | 20 |" in text
+    assert "| SQ_LDS_BANK_CONFLICT | 6 |" in text
+    assert "elementwise" not in text
